@@ -1,0 +1,97 @@
+/*
+ * libsqa: scaled-dot-product attention forward with decoupled query and
+ * key/value head counts, for AMD Instinct MI355X (gfx950).
+ *
+ * One call, sqa_attn_fwd, computes for every batch b, query head h and
+ * query position i
+ *
+ *     out[b,i,h,:] = sum_j softmax_j( scale * <q[b,i,h,:], k[b,j,g,:]> ) v[b,j,g,:]
+ *
+ * where g = floor(h / (H_q / H_kv)) is the key/value head that query head h
+ * shares, and j runs over all S positions (causal = 0) or over j <= i
+ * (causal = 1).
+ *
+ * Sources:
+ *   - Sparse Query Attention ("Sparse Query Attention (SQA): A
+ *     Computationally Efficient Attention Mechanism with Query Heads
+ *     Reduction", abstract): SQA lowers the number of query heads H_q, not
+ *     the number of key/value heads, and the score and P.V work falls in
+ *     proportion to H_q.  The arithmetic per head is unchanged.
+ *   - Grouped heads ("Paper explainer: GQA - Grouped-Query Attention",
+ *     section on MHA/MQA/GQA with the GQA equations and the grouping
+ *     figure): H_kv groups of H_q/H_kv consecutive query heads, each group
+ *     reading one key/value head.  H_kv = H_q is MHA, H_kv = 1 is MQA.  The
+ *     page's PyTorch module asserts that the head count is divisible by the
+ *     group count.
+ *   - The attention call itself (same page, PyTorch module): softmax of the
+ *     scaled scores times V, with is_causal giving the lower-triangular mask.
+ *
+ * Layout.  All four tensors are dense and contiguous in BSHD order: element
+ * (b, s, h, e) sits at ((b*S + s)*H + h)*d + e, with H = H_q for q and out
+ * and H = H_kv for k and v.  This is the layout of the projections before the
+ * page's transpose, so no transpose is needed on either side.
+ *
+ * Ownership.  The caller allocates and owns every buffer (device memory).
+ * The library keeps no state, allocates nothing, and only enqueues work on
+ * `stream` (the null stream is allowed); the call returns before the work is
+ * done.  It is safe to call from several host threads at once.
+ */
+#ifndef SQA_H
+#define SQA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Opaque HIP stream handle (same type as hipStream_t). */
+typedef struct ihipStream_t* sqa_stream_t;
+
+typedef enum {
+  SQA_OK = 0,
+  SQA_ERR_INVALID_ARGUMENT = 1, /* a documented precondition does not hold */
+  SQA_ERR_UNSUPPORTED = 2,      /* valid arguments this build has no kernel for */
+  SQA_ERR_HIP = 3               /* the HIP runtime refused the launch */
+} sqa_status;
+
+typedef enum {
+  SQA_BF16 = 0, /* bf16 in and out, fp32 accumulation, bf16 MFMA */
+  SQA_FP32 = 1  /* fp32 in and out, fp32 arithmetic */
+} sqa_dtype;
+
+/*
+ * Attention forward.
+ *
+ *   q    [B, S, H_q,  d]   device pointer, dtype elements, 16-byte aligned
+ *   k    [B, S, H_kv, d]   device pointer, dtype elements, 16-byte aligned
+ *   v    [B, S, H_kv, d]   device pointer, dtype elements, 16-byte aligned
+ *   out  [B, S, H_q,  d]   device pointer, written in full; must not
+ *                          overlap q, k or v
+ *   B, S       batch size and sequence length (queries and keys have the
+ *              same length S); B*S == 0 is a successful no-op
+ *   H_q, H_kv  query and key/value head counts: H_q >= H_kv >= 1 and
+ *              H_q % H_kv == 0
+ *   d          head dimension: 32, 64 or 128
+ *   scale      finite multiplier of the scores (1/sqrt(d) is usual)
+ *   causal     0 = every query sees all S keys; 1 = query i sees keys j <= i
+ *   stream     HIP stream to enqueue on (NULL = null stream)
+ *
+ * Returns SQA_OK after enqueueing.  SQA_ERR_INVALID_ARGUMENT and
+ * SQA_ERR_UNSUPPORTED are decided from the arguments alone, before any HIP
+ * call, and leave out untouched.  SQA_ERR_HIP reports a launch the runtime
+ * refused.  Faults during execution surface at the caller's next
+ * synchronisation on the stream.
+ */
+sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, void* out, int64_t B,
+                        int64_t S, int32_t H_q, int32_t H_kv, int32_t d, sqa_dtype dtype,
+                        float scale, int causal, sqa_stream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* sqa_status_string(sqa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SQA_H */

@@ -1,0 +1,80 @@
+"""Oracle for decoupled-head attention: plain fp64 CPU definition.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  The product path
+(the HIP library and its binding) never calls it and shares no code with it.
+
+The arithmetic lives in ``sqa_oracle.c``; its header states what it computes
+and which passage of the source pages each step follows.  This module only
+marshals arguments.
+
+Parity status: every function here is pinned by the not-gpu tests in
+tests/test_oracle_pins.py (closed forms, invariants, a library routine and a
+hand-derived fixture); none is "parity unpinned".
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from .build import build, lib_path
+
+_lib = None
+
+_DTYPE_CODE = {np.dtype(np.uint16): 0, np.dtype(np.float32): 1, np.dtype(np.float64): 2}
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            build()
+        lib = ctypes.CDLL(path)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        lib.sqa_oracle_fwd.restype = ctypes.c_int
+        lib.sqa_oracle_fwd.argtypes = [vp, vp, vp, ctypes.c_int, vp, i64, i64, i32, i32, i32,
+                                       ctypes.c_double, ctypes.c_int, vp, i64, ctypes.c_int, vp]
+        _lib = lib
+    return _lib
+
+
+def attention(q, k, v, scale, causal=False, rows=None, n_threads=0, return_pairs=False):
+    """fp64 attention output.
+
+    q: [B, S, H_q, d]; k, v: [B, S, H_kv, d]; all the same dtype: uint16
+    (raw bf16 bits), float32 or float64.  `scale` is used as a double.
+    rows: optional query positions; then the result is [B, len(rows), H_q, d]
+    holding those positions only.  Returns float64 (and the number of
+    (b, h, i, j) score terms evaluated if return_pairs).
+    """
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE_CODE:
+        raise TypeError("q, k, v must share one dtype among uint16(bf16 bits), float32, float64")
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be 4-d BSHD arrays")
+    B, S, H_q, d = q.shape
+    if k.shape[:2] != (B, S) or k.shape[3] != d or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    H_kv = k.shape[2]
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n_out = rows.size
+        rows_ptr = ctypes.c_void_p(rows.ctypes.data)
+    else:
+        n_out = S
+        rows_ptr = None
+    out = np.zeros((B, n_out, H_q, d), dtype=np.float64)
+    pairs = ctypes.c_int64(0)
+    rc = _load().sqa_oracle_fwd(
+        ctypes.c_void_p(q.ctypes.data), ctypes.c_void_p(k.ctypes.data), ctypes.c_void_p(v.ctypes.data),
+        _DTYPE_CODE[q.dtype], ctypes.c_void_p(out.ctypes.data), B, S, H_q, H_kv, d, float(scale),
+        1 if causal else 0, rows_ptr, n_out if rows is not None else 0, int(n_threads),
+        ctypes.byref(pairs))
+    if rc == -1:
+        raise ValueError("oracle: invalid arguments")
+    if rc != 0:
+        raise MemoryError("oracle: allocation failed")
+    return (out, pairs.value) if return_pairs else out

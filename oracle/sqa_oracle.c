@@ -1,0 +1,140 @@
+/*
+ * Oracle for decoupled-head scaled-dot-product attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product path never
+ * calls it, and it shares no code, header, table or helper with the HIP
+ * library.
+ *
+ * What it computes (plain definition, fp64, no blocking and no fusion):
+ *
+ *   - Sparse Query Attention (SQA abstract, "Sparse Query Attention (SQA): A
+ *     Computationally Efficient Attention Mechanism with Query Heads
+ *     Reduction"): the attention arithmetic is the ordinary one; SQA only
+ *     changes how many query heads there are.  Query and key/value head
+ *     counts are therefore independent arguments H_q and H_kv.
+ *   - Head sharing ("Paper explainer: GQA - Grouped-Query Attention", section
+ *     on the relation between MHA, MQA and GQA, the GQA equations and the
+ *     grouping figure): the H_q query heads form H_kv groups of
+ *     R = H_q / H_kv consecutive heads, and every head of group g reads K/V
+ *     head g.  So query head h reads K/V head floor(h / R).  The same page's
+ *     PyTorch module expands K/V with unsqueeze/expand/reshape, which puts
+ *     K/V head g at query heads g*R ... g*R+R-1: the same map.
+ *   - The attention itself (same page, PyTorch module, call to
+ *     scaled_dot_product_attention with is_causal): per query row i,
+ *     scores s_j = scale * <q_i, k_j>, weights softmax over j, output
+ *     sum_j w_j v_j.  Written as on the quantum-attention review ("Beyond
+ *     Classical Attention: Quantum Attention for Scalable Computation",
+ *     proposed-method section): o = D(A)^-1 A V with A = exp(scores) and
+ *     D the diagonal of row sums.
+ *   - Causal: with equal query and key lengths, row i sees keys j <= i.
+ *
+ * Reading taken where the pages are silent: the row maximum is subtracted
+ * before exponentiation (p_j = exp(s_j - m)).  In exact arithmetic this
+ * leaves D(A)^-1 A V unchanged, because numerator and denominator are both
+ * multiplied by exp(-m); it only keeps exp() from overflowing.
+ *
+ * Layout: all tensors dense BSHD, element (b, s, h, e) at ((b*S+s)*H+h)*d+e.
+ * Input dtype code: 0 = bf16 (raw bits), 1 = fp32, 2 = fp64.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* bf16 -> fp64: the bf16 bits are the upper half of an fp32; exact. */
+static double load_elem(const void* p, int dtype, int64_t idx) {
+  if (dtype == 0) {
+    uint32_t u = (uint32_t)((const uint16_t*)p)[idx] << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+  }
+  if (dtype == 1) return (double)((const float*)p)[idx];
+  return ((const double*)p)[idx];
+}
+
+/*
+ * out: fp64, [B, n_out, H_q, d] where n_out = S if rows == NULL, else n_rows
+ *      and output row r holds query position rows[r].
+ * pairs_out (nullable): number of (b, h, i, j) score terms evaluated.
+ * n_threads <= 0 uses the OpenMP default.
+ * Returns 0 on success, -1 on invalid arguments, -2 if memory is short.
+ */
+int sqa_oracle_fwd(const void* q, const void* k, const void* v, int dtype, double* out,
+                   int64_t B, int64_t S, int32_t H_q, int32_t H_kv, int32_t d, double scale,
+                   int causal, const int64_t* rows, int64_t n_rows, int n_threads,
+                   int64_t* pairs_out) {
+  if (B < 0 || S < 0 || H_q < 1 || H_kv < 1 || d < 1) return -1;
+  if (H_q % H_kv != 0) return -1;
+  if (dtype < 0 || dtype > 2) return -1;
+  if (causal != 0 && causal != 1) return -1;
+  const int64_t n_out = rows ? n_rows : S;
+  if (n_out < 0) return -1;
+  if (rows)
+    for (int64_t r = 0; r < n_rows; ++r)
+      if (rows[r] < 0 || rows[r] >= S) return -1;
+  if (pairs_out) *pairs_out = 0;
+  const int64_t items = B * n_out * (int64_t)H_q;
+  if (items == 0) return 0;
+
+  const int32_t R = H_q / H_kv;
+  int64_t pairs = 0;
+  int failed = 0;
+#ifdef _OPENMP
+  if (n_threads <= 0) n_threads = omp_get_max_threads();
+#else
+  n_threads = 1;
+#endif
+
+#pragma omp parallel num_threads(n_threads) reduction(+ : pairs)
+  {
+    double* p = (double*)malloc((size_t)(S > 0 ? S : 1) * sizeof(double));
+    double* acc = (double*)malloc((size_t)d * sizeof(double));
+    if (!p || !acc) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < items; ++t) {
+      if (!p || !acc) continue;
+      const int64_t b = t / (n_out * H_q);
+      const int64_t r = (t / H_q) % n_out;
+      const int32_t h = (int32_t)(t % H_q);
+      const int64_t i = rows ? rows[r] : r;
+      const int32_t g = h / R; /* K/V head shared by query head h */
+      const int64_t last = causal ? i : S - 1;
+      const int64_t q_off = ((b * S + i) * H_q + h) * (int64_t)d;
+
+      /* scores s_j = scale * <q_i, k_j> */
+      double m = -INFINITY;
+      for (int64_t j = 0; j <= last; ++j) {
+        const int64_t k_off = ((b * S + j) * H_kv + g) * (int64_t)d;
+        double dot = 0.0;
+        for (int32_t e = 0; e < d; ++e) dot += load_elem(q, dtype, q_off + e) * load_elem(k, dtype, k_off + e);
+        p[j] = scale * dot;
+        if (p[j] > m) m = p[j];
+      }
+      /* A_ij = exp(s_j - m); D_ii = sum_j A_ij; o = D^-1 A V */
+      double l = 0.0;
+      for (int32_t e = 0; e < d; ++e) acc[e] = 0.0;
+      for (int64_t j = 0; j <= last; ++j) {
+        const double a = exp(p[j] - m);
+        l += a;
+        const int64_t v_off = ((b * S + j) * H_kv + g) * (int64_t)d;
+        for (int32_t e = 0; e < d; ++e) acc[e] += a * load_elem(v, dtype, v_off + e);
+      }
+      double* o = out + ((b * n_out + r) * H_q + h) * (int64_t)d;
+      for (int32_t e = 0; e < d; ++e) o[e] = acc[e] / l;
+      pairs += last + 1;
+    }
+    free(p);
+    free(acc);
+  }
+  if (failed) return -2;
+  if (pairs_out) *pairs_out = pairs;
+  return 0;
+}

@@ -1,0 +1,293 @@
+"""Pins for the oracle: facts fixed by the pages or by mathematics.
+
+None of these re-types the oracle's loop.  They check it against hand-derived
+closed forms (tests/golden), a library routine (torch's CPU
+scaled_dot_product_attention in fp64, the call the GQA explainer's PyTorch
+module makes), algebraic invariants of softmax attention, and the special
+cases the pages name (G = H is MHA, G = 1 is MQA).  Each is chosen so that a
+plausible slip in the oracle (a wrong head map, a transposed score, a causal
+mask off by one, a dropped scale, a missing max shift, bad bf16 decoding)
+fails at least one of them.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import inputs
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.txt")
+
+
+def _num(tok):
+    val = 1.0
+    for factor in tok.split("*"):
+        if factor == "ln2":
+            val *= math.log(2.0)
+        else:
+            val *= float(Fraction(factor))
+    return val
+
+
+def _golden_cases():
+    cases, cur, key = [], None, None
+    with open(GOLDEN) as f:
+        for raw in f:
+            line = raw.strip()
+            if not line or line.startswith("#"):
+                continue
+            parts = line.split()
+            if parts[0] == "case":
+                cur = {"name": parts[1]}
+            elif parts[0] == "shape":
+                cur["shape"] = tuple(int(x) for x in parts[1:])
+            elif parts[0] in ("scale", "causal"):
+                cur[parts[0]] = _num(parts[1])
+            elif parts[0] in ("q", "k", "v", "out"):
+                key = parts[0]
+            elif parts[0] == "end":
+                cases.append(cur)
+            else:
+                cur[key] = np.array([_num(t) for t in parts], dtype=np.float64)
+    return cases
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_hand_derived_cases(case):
+    B, S, H_q, H_kv, d = case["shape"]
+    q = case["q"].reshape(B, S, H_q, d)
+    k = case["k"].reshape(B, S, H_kv, d)
+    v = case["v"].reshape(B, S, H_kv, d)
+    out = oracle.attention(q, k, v, case["scale"], causal=bool(case["causal"]))
+    np.testing.assert_allclose(out.ravel(), case["out"], rtol=1e-14, atol=1e-14)
+
+
+def _rand(rng, B, S, H, d, std=1.0):
+    return rng.standard_normal((B, S, H, d)) * std
+
+
+def _torch_sdpa(q, k, v, scale, causal):
+    """torch CPU fp64 SDPA on K/V expanded to the query heads (BHSD)."""
+    R = q.shape[2] // k.shape[2]
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(R, dim=1)
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(R, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq.contiguous(), tk.contiguous(), tv.contiguous(), is_causal=causal, scale=scale)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,S,H_q,H_kv,d", [(1, 7, 4, 2, 8), (2, 13, 6, 3, 5), (1, 33, 8, 1, 16),
+                                             (2, 9, 3, 3, 4)])
+def test_matches_torch_sdpa_fp64(B, S, H_q, H_kv, d, causal):
+    rng = np.random.default_rng(1000 + S * 7 + H_q)
+    q, k, v = _rand(rng, B, S, H_q, d), _rand(rng, B, S, H_kv, d), _rand(rng, B, S, H_kv, d)
+    scale = 0.37
+    ours = oracle.attention(q, k, v, scale, causal=causal)
+    ref = _torch_sdpa(q, k, v, scale, causal)
+    np.testing.assert_allclose(ours, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_textbook_row_normalised_form_without_shift():
+    """o = D(A)^-1 A V with A = exp(scale Q K^T), masked entries 0, no max shift."""
+    rng = np.random.default_rng(7)
+    for causal in (False, True):
+        q, k, v = _rand(rng, 1, 11, 2, 6), _rand(rng, 1, 11, 2, 6), _rand(rng, 1, 11, 2, 6)
+        ours = oracle.attention(q, k, v, 0.5, causal=causal)
+        for h in range(2):
+            A = np.exp(0.5 * (q[0, :, h, :] @ k[0, :, h, :].T))
+            if causal:
+                A = np.tril(A)
+            O = np.diag(1.0 / A.sum(axis=1)) @ A @ v[0, :, h, :]
+            np.testing.assert_allclose(ours[0, :, h, :], O, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_equals_mha_on_repeated_kv(causal):
+    """GQA(q, k, v) == MHA(q, expand(k), expand(v)), expand as in the page's module."""
+    rng = np.random.default_rng(11)
+    B, S, H_q, H_kv, d = 2, 17, 8, 2, 8
+    q, k, v = _rand(rng, B, S, H_q, d), _rand(rng, B, S, H_kv, d), _rand(rng, B, S, H_kv, d)
+    R = H_q // H_kv
+    # unsqueeze/expand/reshape along the head axis: K/V head g -> heads gR..gR+R-1
+    k_rep = np.repeat(k, R, axis=2)
+    v_rep = np.repeat(v, R, axis=2)
+    grouped = oracle.attention(q, k, v, 0.3, causal=causal)
+    mha = oracle.attention(q, k_rep, v_rep, 0.3, causal=causal)
+    assert np.array_equal(grouped, mha)
+    # the interleaved map (h -> h mod H_kv) is a different function
+    inter = oracle.attention(q, np.tile(k, (1, 1, R, 1)), np.tile(v, (1, 1, R, 1)), 0.3, causal=causal)
+    assert np.abs(inter - grouped).max() > 1e-3
+
+
+def test_mqa_every_head_reads_the_single_kv_head():
+    rng = np.random.default_rng(12)
+    B, S, H_q, d = 1, 10, 5, 4
+    q, k, v = _rand(rng, B, S, H_q, d), _rand(rng, B, S, 1, d), _rand(rng, B, S, 1, d)
+    full = oracle.attention(q, k, v, 0.7)
+    for h in range(H_q):
+        single = oracle.attention(q[:, :, h:h + 1, :].copy(), k, v, 0.7)
+        assert np.array_equal(full[:, :, h:h + 1, :], single)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_scores_give_mean_of_v(causal):
+    rng = np.random.default_rng(13)
+    B, S, H_q, H_kv, d = 2, 9, 4, 2, 3
+    q = np.zeros((B, S, H_q, d))
+    k, v = _rand(rng, B, S, H_kv, d), _rand(rng, B, S, H_kv, d)
+    out = oracle.attention(q, k, v, 1.3, causal=causal)
+    for h in range(H_q):
+        g = h // (H_q // H_kv)
+        if causal:
+            expect = np.cumsum(v[:, :, g, :], axis=1) / np.arange(1, S + 1)[None, :, None]
+        else:
+            expect = np.broadcast_to(v[:, :, g, :].mean(axis=1, keepdims=True), (B, S, d))
+        np.testing.assert_allclose(out[:, :, h, :], expect, rtol=1e-13, atol=1e-14)
+
+
+def test_causal_row_zero_is_v0():
+    rng = np.random.default_rng(14)
+    B, S, H_q, H_kv, d = 2, 6, 6, 3, 5
+    q, k, v = _rand(rng, B, S, H_q, d, 5.0), _rand(rng, B, S, H_kv, d, 5.0), _rand(rng, B, S, H_kv, d)
+    out = oracle.attention(q, k, v, 1.0, causal=True)
+    for h in range(H_q):
+        assert np.array_equal(out[:, 0, h, :], v[:, 0, h // 2, :])
+
+
+def test_causal_row_equals_noncausal_on_prefix():
+    """Row i of the causal result is the non-causal result on positions 0..i."""
+    rng = np.random.default_rng(15)
+    B, S, H_q, H_kv, d = 1, 12, 2, 1, 4
+    q, k, v = _rand(rng, B, S, H_q, d), _rand(rng, B, S, H_kv, d), _rand(rng, B, S, H_kv, d)
+    causal = oracle.attention(q, k, v, 0.9, causal=True)
+    for i in range(S):
+        pre = oracle.attention(q[:, :i + 1].copy(), k[:, :i + 1].copy(), v[:, :i + 1].copy(), 0.9)
+        np.testing.assert_allclose(causal[:, i], pre[:, i], rtol=1e-14, atol=1e-15)
+
+
+def test_key_shift_invariance_forces_max_subtraction():
+    """Adding u to every key adds the same q.u to each score of a row: no change.
+
+    With |scale * q.u| near 1000, exp() overflows fp64 unless the row maximum
+    is subtracted first, so this also pins the stabilisation.
+    """
+    rng = np.random.default_rng(16)
+    B, S, H, d = 1, 8, 2, 4
+    q = np.abs(_rand(rng, B, S, H, d)) + 1.0
+    k, v = _rand(rng, B, S, H, d), _rand(rng, B, S, H, d)
+    base = oracle.attention(q, k, v, 1.0)
+    shifted = oracle.attention(q, k + 300.0, v, 1.0)
+    assert np.isfinite(shifted).all()
+    np.testing.assert_allclose(shifted, base, rtol=1e-9, atol=1e-9)
+
+
+def test_affine_values():
+    rng = np.random.default_rng(17)
+    q, k, v = _rand(rng, 1, 10, 4, 3), _rand(rng, 1, 10, 2, 3), _rand(rng, 1, 10, 2, 3)
+    for causal in (False, True):
+        a = oracle.attention(q, k, v, 0.8, causal=causal)
+        b = oracle.attention(q, k, 2.5 * v - 1.75, 0.8, causal=causal)
+        np.testing.assert_allclose(b, 2.5 * a - 1.75, rtol=1e-12, atol=1e-12)
+
+
+def test_permutations_noncausal():
+    rng = np.random.default_rng(18)
+    q, k, v = _rand(rng, 1, 15, 2, 4), _rand(rng, 1, 15, 1, 4), _rand(rng, 1, 15, 1, 4)
+    base = oracle.attention(q, k, v, 0.6)
+    perm = rng.permutation(15)
+    keys_permuted = oracle.attention(q, k[:, perm].copy(), v[:, perm].copy(), 0.6)
+    np.testing.assert_allclose(keys_permuted, base, rtol=1e-13, atol=1e-14)
+    rows_permuted = oracle.attention(q[:, perm].copy(), k, v, 0.6)
+    np.testing.assert_allclose(rows_permuted, base[:, perm], rtol=1e-13, atol=1e-14)
+
+
+def test_single_key_and_two_key_closed_forms():
+    rng = np.random.default_rng(19)
+    q, k, v = _rand(rng, 1, 1, 3, 4), _rand(rng, 1, 1, 3, 4), _rand(rng, 1, 1, 3, 4)
+    assert np.array_equal(oracle.attention(q, k, v, 2.0), v)
+    q, k, v = _rand(rng, 1, 2, 1, 3), _rand(rng, 1, 2, 1, 3), _rand(rng, 1, 2, 1, 3)
+    out = oracle.attention(q, k, v, 0.25)
+    for i in range(2):
+        s0 = 0.25 * float(q[0, i, 0] @ k[0, 0, 0])
+        s1 = 0.25 * float(q[0, i, 0] @ k[0, 1, 0])
+        w1 = 1.0 / (1.0 + math.exp(s0 - s1))
+        expect = (1.0 - w1) * v[0, 0, 0] + w1 * v[0, 1, 0]
+        np.testing.assert_allclose(out[0, i, 0], expect, rtol=1e-13, atol=1e-14)
+
+
+def test_peaked_row_picks_its_value():
+    """One key far above the rest: the output tends to that key's value."""
+    rng = np.random.default_rng(20)
+    q = np.ones((1, 4, 1, 2))
+    k = _rand(rng, 1, 4, 1, 2) * 0.01
+    k[0, 2, 0, :] = 40.0
+    v = _rand(rng, 1, 4, 1, 2)
+    out = oracle.attention(q, k, v, 1.0)
+    np.testing.assert_allclose(out[0, :, 0, :], np.broadcast_to(v[0, 2, 0, :], (4, 2)), atol=1e-30, rtol=1e-30)
+
+
+def test_batches_are_independent():
+    rng = np.random.default_rng(21)
+    q, k, v = _rand(rng, 3, 6, 2, 4), _rand(rng, 3, 6, 2, 4), _rand(rng, 3, 6, 2, 4)
+    full = oracle.attention(q, k, v, 0.5, causal=True)
+    for b in range(3):
+        one = oracle.attention(q[b:b + 1].copy(), k[b:b + 1].copy(), v[b:b + 1].copy(), 0.5, causal=True)
+        assert np.array_equal(full[b:b + 1], one)
+
+
+def test_row_subset_equals_full_rows():
+    rng = np.random.default_rng(22)
+    q, k, v = _rand(rng, 2, 20, 4, 4), _rand(rng, 2, 20, 2, 4), _rand(rng, 2, 20, 2, 4)
+    rows = np.array([0, 5, 19, 7])
+    for causal in (False, True):
+        full = oracle.attention(q, k, v, 0.5, causal=causal)
+        sub = oracle.attention(q, k, v, 0.5, causal=causal, rows=rows)
+        assert np.array_equal(sub, full[:, rows])
+
+
+def test_bf16_inputs_decode_exactly():
+    """bf16 bits give the same result as their exact fp32 widening."""
+    bits_q = inputs.normal(5, 0, (1, 9, 4, 8), "bf16", 0.5)
+    bits_k = inputs.normal(5, 1, (1, 9, 2, 8), "bf16", 0.5)
+    bits_v = inputs.normal(5, 2, (1, 9, 2, 8), "bf16", 0.5)
+    # decode by hand: sign, exponent and mantissa of each bf16 value
+    def decode(bits):
+        b = bits.astype(np.int64)
+        sign = np.where(b >> 15, -1.0, 1.0)
+        exp = (b >> 7) & 0xFF
+        man = b & 0x7F
+        return sign * np.where(exp == 0, man / 128.0 * 2.0 ** -126, (1 + man / 128.0) * 2.0 ** (exp - 127))
+    a = oracle.attention(bits_q, bits_k, bits_v, 0.35, causal=True)
+    b = oracle.attention(decode(bits_q), decode(bits_k), decode(bits_v), 0.35, causal=True)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_pair_count_is_the_flop_model(causal):
+    rng = np.random.default_rng(23)
+    B, S, H_q, H_kv, d = 2, 11, 6, 2, 3
+    q, k, v = _rand(rng, B, S, H_q, d), _rand(rng, B, S, H_kv, d), _rand(rng, B, S, H_kv, d)
+    _, pairs = oracle.attention(q, k, v, 1.0, causal=causal, return_pairs=True)
+    expect = B * H_q * (S * (S + 1) // 2 if causal else S * S)
+    assert pairs == expect
+
+
+def test_rejects_non_divisible_heads():
+    q = np.zeros((1, 2, 3, 4))
+    k = np.zeros((1, 2, 2, 4))
+    with pytest.raises(ValueError):
+        oracle.attention(q, k, k, 1.0)
+
+
+def test_thread_count_does_not_change_result():
+    rng = np.random.default_rng(24)
+    q, k, v = _rand(rng, 1, 40, 4, 8), _rand(rng, 1, 40, 2, 8), _rand(rng, 1, 40, 2, 8)
+    a = oracle.attention(q, k, v, 0.5, causal=True, n_threads=1)
+    b = oracle.attention(q, k, v, 0.5, causal=True, n_threads=4)
+    assert np.array_equal(a, b)
