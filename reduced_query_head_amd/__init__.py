@@ -1,0 +1,92 @@
+"""Python binding of libsqa: decoupled-head attention forward on MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``lib/libsqa.so`` (sources in ``csrc/``, C-ABI in
+``include/sqa.h``).  There is no CPU fallback; if the library is missing the
+import of the native entry points fails loudly.
+"""
+import ctypes
+import math
+import os
+
+from ._build import build, lib_path
+
+SQA_OK, SQA_ERR_INVALID_ARGUMENT, SQA_ERR_UNSUPPORTED, SQA_ERR_HIP = 0, 1, 2, 3
+SQA_BF16, SQA_FP32 = 0, 1
+
+_lib = None
+
+
+class SqaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def load_library(path=None):
+    """Load libsqa.so (build it first if it is absent) and declare its symbols."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or lib_path()
+    if not os.path.exists(path):
+        build()
+    lib = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.sqa_attn_fwd.restype = ctypes.c_int
+    lib.sqa_attn_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, ctypes.c_int, ctypes.c_float,
+                                 ctypes.c_int, vp]
+    lib.sqa_status_string.restype = ctypes.c_char_p
+    lib.sqa_status_string.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load_library().sqa_status_string(status).decode()
+
+
+def attn_fwd_raw(q, k, v, out, B, S, H_q, H_kv, d, dtype, scale, causal, stream):
+    """Direct call of sqa_attn_fwd with integer device addresses; returns the status."""
+    return load_library().sqa_attn_fwd(q, k, v, out, B, S, H_q, H_kv, d, dtype, scale, int(causal),
+                                       stream)
+
+
+def attn_fwd(q, k, v, out=None, scale=None, causal=False, stream=None):
+    """out[b,i,h] = softmax_j(scale * q[b,i,h].k[b,j,h//R]) . v[b,j,h//R].
+
+    q: [B, S, H_q, d], k and v: [B, S, H_kv, d], torch tensors on the GPU,
+    contiguous, all bfloat16 or all float32.  scale defaults to 1/sqrt(d).
+    The kernel is enqueued on `stream` (default: torch's current stream).
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-d GPU tensor")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    if q.dtype == torch.bfloat16:
+        dtype = SQA_BF16
+    elif q.dtype == torch.float32:
+        dtype = SQA_FP32
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, S, H_q, d = q.shape
+    if tuple(k.shape[:2]) != (B, S) or k.shape[3] != d or k.shape != v.shape:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    H_kv = k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous GPU tensor shaped and typed like q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, S, H_q, H_kv, d,
+                      dtype, float(scale), causal, handle)
+    if st != SQA_OK:
+        raise SqaError(st, status_string(st))
+    return out

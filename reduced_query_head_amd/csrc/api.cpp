@@ -1,0 +1,91 @@
+// C-ABI entry points of libsqa: argument validation and kernel dispatch.
+// Every check runs before any HIP call, so a rejected call has no effect.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/sqa.h"
+#include "launch.h"
+
+#define SQA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+bool ranges_overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)b_bytes && b0 < a0 + (uintptr_t)a_bytes;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+}  // namespace
+
+SQA_API const char* sqa_status_string(sqa_status status) {
+  switch (status) {
+    case SQA_OK: return "success";
+    case SQA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SQA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SQA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+SQA_API sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, void* out, int64_t B,
+                                int64_t S, int32_t H_q, int32_t H_kv, int32_t d, sqa_dtype dtype,
+                                float scale, int causal, sqa_stream_t stream) {
+  // head counts: groups of H_q / H_kv query heads share one K/V head, so the
+  // group count must divide the head count (GQA module's assertion)
+  if (B < 0 || S < 0 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0) return SQA_ERR_INVALID_ARGUMENT;
+  if (dtype != SQA_BF16 && dtype != SQA_FP32) return SQA_ERR_INVALID_ARGUMENT;
+  if (causal != 0 && causal != 1) return SQA_ERR_INVALID_ARGUMENT;
+  if (!isfinite(scale)) return SQA_ERR_INVALID_ARGUMENT;
+  if (d < 1) return SQA_ERR_INVALID_ARGUMENT;
+  if (B == 0 || S == 0) return SQA_OK;
+  if (!q || !k || !v || !out) return SQA_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15u) return SQA_ERR_INVALID_ARGUMENT;
+
+  const int64_t elem = dtype == SQA_BF16 ? 2 : 4;
+  int64_t rows, q_elems, kv_elems, q_bytes, kv_bytes;
+  if (!mul_ok(B, S, &rows) || !mul_ok(rows, (int64_t)H_q * d, &q_elems) ||
+      !mul_ok(rows, (int64_t)H_kv * d, &kv_elems) || !mul_ok(q_elems, elem, &q_bytes) ||
+      !mul_ok(kv_elems, elem, &kv_bytes))
+    return SQA_ERR_INVALID_ARGUMENT;
+  if (ranges_overlap(out, q_bytes, q, q_bytes) || ranges_overlap(out, q_bytes, k, kv_bytes) ||
+      ranges_overlap(out, q_bytes, v, kv_bytes))
+    return SQA_ERR_INVALID_ARGUMENT;
+
+  if (d != 32 && d != 64 && d != 128) return SQA_ERR_UNSUPPORTED;
+  // kernels index positions with 32-bit integers
+  if (S > (int64_t)1 << 30) return SQA_ERR_UNSUPPORTED;
+  if (dtype == SQA_BF16) {
+    if (sqa::bf16_grid_size(B, S, H_q, H_kv) > INT32_MAX) return SQA_ERR_UNSUPPORTED;
+  } else {
+    if ((rows * H_q + 255) / 256 > INT32_MAX) return SQA_ERR_UNSUPPORTED;
+  }
+
+  sqa::LaunchArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.B = B;
+  a.S = S;
+  a.H_q = H_q;
+  a.H_kv = H_kv;
+  a.d = d;
+  a.dtype = dtype == SQA_BF16 ? 0 : 1;
+  // scores enter the softmax as scale * s * log2(e) so that exp2 can be used;
+  // a negative scale is folded into q (exact for bf16: a sign flip)
+  const float log2e = 1.4426950408889634f;
+  const float mag = fabsf(scale);
+  a.c = mag > 0.f ? mag * log2e : 1e-30f;
+  if (!isfinite(a.c)) return SQA_ERR_INVALID_ARGUMENT;
+  a.negate_q = scale < 0.f;
+  a.causal = causal;
+  a.stream = (void*)stream;
+  return sqa::launch_attn_fwd(a) == hipSuccess ? SQA_OK : SQA_ERR_HIP;
+}

@@ -1,0 +1,422 @@
+// Decoupled-head attention forward for gfx950 (MI355X, CDNA4).
+//
+// Computes, for every batch b, query head h and position i,
+//   out[b,i,h,:] = sum_j softmax_j(scale * <q[b,i,h,:], k[b,j,g,:]>) v[b,j,g,:]
+// with g = floor(h / R), R = H_q / H_kv: the head sharing of grouped-query
+// attention ("Paper explainer: GQA - Grouped-Query Attention", the GQA
+// equations and the grouping figure; the PyTorch module's expand order), with
+// the query-head count free as in Sparse Query Attention ("Sparse Query
+// Attention (SQA)", abstract).  The softmax is evaluated online over key
+// tiles (running row maximum and row sum), which equals the row-normalised
+// form D(A)^-1 A V exactly in real arithmetic.
+//
+// bf16 kernel design (one workgroup = WAVES waves of 64 lanes):
+//  * A workgroup owns one key/value group (b, g) and WAVES "items"; an item
+//    is 32 consecutive query positions of one query head of that group.
+//    Items are ordered position-block-major, head-minor, so the waves of a
+//    workgroup cover the same positions for up to WAVES heads, and every
+//    K/V tile staged in LDS feeds all of them.
+//  * Scores are computed transposed, S^T = K Q^T, with
+//    v_mfma_f32_32x32x16_bf16: keys run along M, queries along N.  Each lane
+//    then holds 16 scores of a single query per 32-key block, so the row
+//    maximum and row sum are in-register reductions plus one
+//    v_permlane32_swap between the two lane halves.
+//  * O^T = V^T P^T reuses the score accumulator as the B operand: the lane
+//    that holds P[query][key] for 8 keys is exactly the lane the MFMA wants,
+//    once the MFMA's K index is mapped to the keys in the order the score
+//    accumulator holds them.  V^T comes from LDS with ds_read_b64_tr_b16.
+//  * K and V tiles of 64 keys go global -> LDS directly
+//    (global_load_lds_dwordx4), double-buffered, one barrier per tile.  The
+//    LDS layout XOR-swizzles 16-byte chunks by the row bits so that both the
+//    K operand reads and the transposed V reads are bank-conflict free.
+//  * Causal: tiles above a wave's last row are skipped, diagonal tiles are
+//    masked per element; sequence tails: key rows are clamped for the loads
+//    and masked in the scores, query rows past S are never stored.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace sqa {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+#define SQA_LDS __attribute__((address_space(3)))
+
+constexpr int kKeys = 64;         // keys per K/V tile
+constexpr int kRows = 32;         // query positions per item (one wave)
+
+struct Bf16Params {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  int S;
+  int H_q;
+  int H_kv;
+  int R;
+  int n_groups;          // B * H_kv
+  int n_items;           // R * ceil(S / kRows), items per group
+  int chunks;            // ceil(n_items / WAVES), workgroups per group
+  float c;               // |scale| * log2(e), strictly positive
+  uint32_t q_sign;       // 0x8000 when scale < 0: q is negated on load (exact)
+};
+
+// 16-byte chunk swizzle inside a tile row.  XOR-linear in the low row bits;
+// chosen so that (a) 32 consecutive rows read at one chunk (K operand) and
+// (b) 4 rows x 2 adjacent chunks per 16 lanes (transposed V reads) hit
+// distinct banks.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) {
+    const int r = row & 15;
+    return r ^ ((r & 3) << 2);
+  } else if constexpr (D == 64) {
+    const int r0 = row & 1, r1 = (row >> 1) & 1, r2 = (row >> 2) & 1, r3 = (row >> 3) & 1;
+    return r1 | ((r0 ^ r2) << 1) | ((r0 ^ r1 ^ r3) << 2);
+  } else {
+    return row & 3;
+  }
+}
+
+// element offset of (row, col) inside a swizzled [kKeys][D] tile
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int col) {
+  return row * D + (((col >> 3) ^ swz<D>(row)) << 3) + (col & 7);
+}
+
+__device__ __forceinline__ float wave_pair_max(float x) {
+  // x from lane l and lane l^32 (the other half of the wave)
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float wave_pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Stage one [kKeys][D] tile of K or V for group (b, g) into LDS.  Each wave
+// issues kKeys*D/8/64/WAVES global->LDS copies of 16 bytes per lane; lane i of
+// copy u fills LDS chunk u*64+i, so the global chunk it fetches is the one
+// the swizzle places there.  Rows at or past S are clamped to S-1 (in
+// bounds); their scores are masked and their probabilities are exactly 0.
+template <int D, int WAVES>
+__device__ __forceinline__ void stage_tile(const uint16_t* head_base, int64_t row_stride, int kv0,
+                                           int S, SQA_LDS uint16_t* tile, int wave, int lane) {
+  constexpr int CH = D / 8;
+  constexpr int COPIES = kKeys * CH / 64;
+  static_assert(COPIES % WAVES == 0, "tile copies must split evenly over the waves");
+#pragma unroll
+  for (int u0 = 0; u0 < COPIES; u0 += WAVES) {
+    const int u = u0 + wave;
+    const int pc = u * 64 + lane;
+    const int row = pc / CH;
+    const int chunk = (pc % CH) ^ swz<D>(row);
+    const int grow = min(kv0 + row, S - 1);
+    const uint16_t* src = head_base + (int64_t)grow * row_stride + chunk * 8;
+    __builtin_amdgcn_global_load_lds((const void*)src, (SQA_LDS void*)(tile + u * 512), 16, 0, 0);
+  }
+}
+
+template <int D, bool CAUSAL, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_bf16(Bf16Params p) {
+  constexpr int KS = D / 16;      // MFMA k-steps over the head dimension
+  constexpr int DB = D / 32;      // 32-row blocks of O^T
+  constexpr int NB = kKeys / 32;  // 32-key blocks per tile
+  constexpr int NT = kKeys / 16;  // 16-key MFMA steps of P.V per tile
+  constexpr int TILE = kKeys * D; // elements per tile
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * TILE];  // K0 K1 V0 V1
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5;     // which half of the wave
+  const int col = lane & 31;      // query column of this lane in S^T / O^T
+  const int S = p.S;
+
+  // workgroup -> (group, chunk).  Consecutive workgroups cycle through the
+  // groups, so with round-robin dispatch over the XCDs each XCD keeps
+  // streaming the same groups' K/V; causal chunks go heaviest first.
+  const int grp = blockIdx.x % p.n_groups;
+  const int ord = blockIdx.x / p.n_groups;
+  const int chunk = CAUSAL ? (p.chunks - 1 - ord) : ord;
+  const int b = grp / p.H_kv;
+  const int g = grp % p.H_kv;
+
+  const int item = chunk * WAVES + wave;
+  const bool active = item < p.n_items;
+  const int pos0 = (item / p.R) * kRows;
+  const int h = g * p.R + item % p.R;
+
+  const int last_item = min(chunk * WAVES + WAVES - 1, p.n_items - 1);
+  const int wg_last_pos = min((last_item / p.R) * kRows + kRows - 1, S - 1);
+  const int n_tiles = CAUSAL ? wg_last_pos / kKeys + 1 : (S + kKeys - 1) / kKeys;
+
+  const int64_t kv_stride = (int64_t)p.H_kv * D;
+  const uint16_t* k_base = p.k + ((int64_t)b * S * p.H_kv + g) * D;
+  const uint16_t* v_base = p.v + ((int64_t)b * S * p.H_kv + g) * D;
+  SQA_LDS uint16_t* lds_k = (SQA_LDS uint16_t*)lds;
+  SQA_LDS uint16_t* lds_v = (SQA_LDS uint16_t*)lds + 2 * TILE;
+
+  // first K/V tile in flight while Q loads
+  stage_tile<D, WAVES>(k_base, kv_stride, 0, S, lds_k, wave, lane);
+  stage_tile<D, WAVES>(v_base, kv_stride, 0, S, lds_v, wave, lane);
+
+  // Q^T as the B operand: lane holds query (pos0 + col), head dims
+  // ks*16 + half*8 ... +7.
+  bf16x8 qf[KS];
+  {
+    const int qrow = min(pos0 + col, S - 1);
+    const uint16_t* qp = p.q + (((int64_t)b * S + qrow) * p.H_q + h) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 raw = *(const u32x4*)(qp + ks * 16);
+      const uint32_t sgn = p.q_sign * 0x10001u;
+      raw ^= (u32x4){sgn, sgn, sgn, sgn};
+      qf[ks] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+
+  // per-lane LDS element offsets (tile-relative), independent of the tile
+  int k_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = tile_off<D>(col, ks * 16 + half * 8);
+  // transposed V reads: lane (within its 16-lane group) supplies the address
+  // of row e = (lane%16)/4 and columns 4*(lane%4) ... +3 of a 4 x 16 block;
+  // the hardware returns to lane i the 4 rows of column i.
+  int v_off[DB][2];
+  {
+    const int grp16 = lane >> 4, i16 = lane & 15, e = i16 >> 2, c4 = i16 & 3;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = 4 * half + 8 * j + e;
+        const int cc = db * 32 + (grp16 & 1) * 16 + 4 * c4;
+        v_off[db][j] = tile_off<D>(row, cc);
+      }
+  }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;
+  const float c = p.c;
+  const int my_q = pos0 + col;
+  const int wave_last = pos0 + kRows - 1;
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int kv0 = t * kKeys;
+    const int buf = t & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile-t copies landed
+    __syncthreads();                      // everyone's copies landed; tile t-1 fully consumed
+    if (t + 1 < n_tiles) {
+      stage_tile<D, WAVES>(k_base, kv_stride, kv0 + kKeys, S, lds_k + (buf ^ 1) * TILE, wave, lane);
+      stage_tile<D, WAVES>(v_base, kv_stride, kv0 + kKeys, S, lds_v + (buf ^ 1) * TILE, wave, lane);
+    }
+    if (!active) continue;
+    if (CAUSAL && kv0 > wave_last) continue;   // whole tile above this wave's rows
+
+    const SQA_LDS uint16_t* kt = lds_k + buf * TILE;
+    const SQA_LDS uint16_t* vt = lds_v + buf * TILE;
+
+    // S^T = K Q^T
+    f32x16 s[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      s[nb] = (f32x16){};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = *(const SQA_LDS bf16x8*)(kt + nb * 32 * D + k_off[ks]);
+        s[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[nb], 0, 0, 0);
+      }
+    }
+
+    // mask: key index of s[nb][r] is kv0 + nb*32 + 8*(r/4) + 4*half + r%4
+    const bool need_mask = (kv0 + kKeys > S) || (CAUSAL && kv0 + kKeys - 1 > pos0);
+    if (need_mask) {
+      const int lim = CAUSAL ? min(my_q, S - 1) : S - 1;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (key > lim) s[nb][r] = -__builtin_inff();
+        }
+    }
+
+    // online softmax in the exp2 domain: p = 2^(c*s - m)
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][r]);
+    mx = wave_pair_max(mx);
+    const float m_new = fmaxf(m_run, mx * c);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    const float neg_m = -m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][r], c, neg_m));
+        s[nb][r] = pv;
+        psum += pv;
+      }
+    l_run = l_run * alpha + psum;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    }
+
+    // O^T += V^T P^T, 16 keys per MFMA.  MFMA k-slot half*8 + e maps to key
+    // 16*(step%2) + 4*half + e (e < 4) or + 8 + 4*half + (e-4) of block step/2,
+    // which is where the score accumulator left them.
+#pragma unroll
+    for (int st = 0; st < NT; ++st) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[st >> 1][(st & 1) * 8 + e];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (SQA_LDS bf16x4*)(vt + st * 16 * D + v_off[db][0]));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (SQA_LDS bf16x4*)(vt + st * 16 * D + v_off[db][1]));
+        const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[db], 0, 0, 0);
+      }
+    }
+  }
+
+  if (!active) return;
+  const int out_pos = pos0 + col;
+  if (out_pos >= S) return;  // lanes l and l^32 share out_pos, so pairs leave together
+  const float inv = 1.0f / wave_pair_sum(l_run);
+  uint16_t* op = p.o + (((int64_t)b * S + out_pos) * p.H_q + h) * D;
+  // O^T[db] register r holds head dim db*32 + 8*(r/4) + 4*half + r%4
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[db][4 * j + e] * inv);
+      *(bf16x4*)(op + db * 32 + 8 * j + 4 * half) = w;
+    }
+}
+
+// fp32 path: one thread per (b, position, head), online softmax over keys in
+// fp32.  Plain VALU arithmetic; meant for exactness checks at small sizes.
+template <int D>
+__global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
+                                                    const float* __restrict__ k,
+                                                    const float* __restrict__ v, float* __restrict__ o,
+                                                    int64_t B, int S, int H_q, int H_kv, int R, float c,
+                                                    int causal) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= B * S * H_q) return;
+  const int h = (int)(t % H_q);
+  const int i = (int)((t / H_q) % S);
+  const int64_t b = t / ((int64_t)H_q * S);
+  const int g = h / R;
+  float qv[D], acc[D];
+  const float* qp = q + t * D;
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    qv[e] = qp[e];
+    acc[e] = 0.f;
+  }
+  float m = -__builtin_inff(), l = 0.f;
+  const int last = causal ? i : S - 1;
+  for (int j = 0; j <= last; ++j) {
+    const float* kp = k + ((b * S + j) * H_kv + g) * D;
+    const float* vp = v + ((b * S + j) * H_kv + g) * D;
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < D; ++e) dot = __builtin_fmaf(qv[e], kp[e], dot);
+    const float x = dot * c;
+    const float m_new = fmaxf(m, x);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    const float pj = __builtin_amdgcn_exp2f(x - m_new);
+    m = m_new;
+    l = l * alpha + pj;
+#pragma unroll
+    for (int e = 0; e < D; ++e) acc[e] = __builtin_fmaf(pj, vp[e], acc[e] * alpha);
+  }
+  const float inv = 1.0f / l;
+  float* op = o + t * D;
+#pragma unroll
+  for (int e = 0; e < D; ++e) op[e] = acc[e] * inv;
+}
+
+constexpr int kWaves = 4;
+
+template <int D, bool CAUSAL>
+hipError_t launch_bf16_t(const LaunchArgs& a) {
+  Bf16Params p;
+  p.q = (const uint16_t*)a.q;
+  p.k = (const uint16_t*)a.k;
+  p.v = (const uint16_t*)a.v;
+  p.o = (uint16_t*)a.out;
+  p.S = (int)a.S;
+  p.H_q = a.H_q;
+  p.H_kv = a.H_kv;
+  p.R = a.H_q / a.H_kv;
+  p.n_groups = (int)(a.B * a.H_kv);
+  const int n_pos_blocks = (int)((a.S + kRows - 1) / kRows);
+  p.n_items = p.R * n_pos_blocks;
+  p.chunks = (p.n_items + kWaves - 1) / kWaves;
+  p.c = a.c;
+  p.q_sign = a.negate_q ? 0x8000u : 0u;
+  const int64_t grid = (int64_t)p.n_groups * p.chunks;
+  hipLaunchKernelGGL((attn_fwd_bf16<D, CAUSAL, kWaves>), dim3((unsigned)grid), dim3(kWaves * 64), 0,
+                     (hipStream_t)a.stream, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_f32_t(const LaunchArgs& a) {
+  const int64_t threads = a.B * a.S * a.H_q;
+  const int64_t blocks = (threads + 255) / 256;
+  // fp32 kernel keeps the sign of scale in c (no bf16 operand to negate)
+  const float c = a.negate_q ? -a.c : a.c;
+  hipLaunchKernelGGL((attn_fwd_f32<D>), dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)a.stream,
+                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out, a.B,
+                     (int)a.S, a.H_q, a.H_kv, a.H_q / a.H_kv, c, a.causal);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t bf16_grid_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv) {
+  const int64_t R = H_q / H_kv;
+  const int64_t items = R * ((S + kRows - 1) / kRows);
+  return B * H_kv * ((items + kWaves - 1) / kWaves);
+}
+
+hipError_t launch_attn_fwd(const LaunchArgs& a) {
+  if (a.dtype == 0) {
+    switch (a.d) {
+      case 32: return a.causal ? launch_bf16_t<32, true>(a) : launch_bf16_t<32, false>(a);
+      case 64: return a.causal ? launch_bf16_t<64, true>(a) : launch_bf16_t<64, false>(a);
+      case 128: return a.causal ? launch_bf16_t<128, true>(a) : launch_bf16_t<128, false>(a);
+    }
+  } else {
+    switch (a.d) {
+      case 32: return launch_f32_t<32>(a);
+      case 64: return launch_f32_t<64>(a);
+      case 128: return launch_f32_t<128>(a);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sqa

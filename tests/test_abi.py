@@ -1,0 +1,71 @@
+"""The C-ABI library loads, exports what include/sqa.h declares, and rejects
+bad arguments before touching the GPU (these calls return before any HIP
+call, so they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import reduced_query_head_amd as sqa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "sqa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sqa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sqa.load_library()
+    names = _declared_functions()
+    assert "sqa_attn_fwd" in names and "sqa_status_string" in names
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in sqa.h but not exported"
+
+
+def test_status_strings():
+    assert sqa.status_string(0) == "success"
+    assert sqa.status_string(1) == "invalid argument"
+    assert sqa.status_string(2) == "unsupported configuration"
+    assert sqa.status_string(3) == "HIP runtime error"
+
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced (rejected first)
+
+
+def _call(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), out=FAKE + (3 << 30), B=1, S=128, H_q=8,
+          H_kv=2, d=128, dtype=0, scale=0.088, causal=0):
+    return sqa.attn_fwd_raw(q, k, v, out, B, S, H_q, H_kv, d, dtype, scale, causal, 0)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(H_q=6, H_kv=4),          # groups must divide heads
+    dict(H_q=2, H_kv=4),          # fewer query heads than K/V heads
+    dict(H_q=0), dict(H_kv=0), dict(B=-1), dict(S=-5), dict(d=0),
+    dict(dtype=7), dict(causal=2),
+    dict(scale=float("inf")), dict(scale=float("nan")), dict(scale=3e38),
+    dict(q=0), dict(k=0), dict(v=0), dict(out=0),
+    dict(q=FAKE + 8),             # misaligned
+    dict(out=FAKE + 64),          # out overlaps q
+    dict(out=FAKE + (1 << 30) + 1024),   # out overlaps k
+])
+def test_invalid_arguments(kw):
+    assert _call(**kw) == sqa.SQA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(d=96), dict(d=256), dict(d=16)])
+def test_unsupported(kw):
+    assert _call(**kw) == sqa.SQA_ERR_UNSUPPORTED
+
+
+def test_sequence_too_long_is_unsupported():
+    far = 1 << 44   # buffers spaced wider than the 2^41-byte tensors
+    assert _call(q=far, k=2 * far, v=3 * far, out=4 * far, S=(1 << 30) + 1) == sqa.SQA_ERR_UNSUPPORTED
+
+
+def test_empty_is_noop():
+    assert _call(B=0, q=0, k=0, v=0, out=0) == sqa.SQA_OK
+    assert _call(S=0, q=0, k=0, v=0, out=0) == sqa.SQA_OK

@@ -1,0 +1,125 @@
+"""GPU parity: the HIP kernels against the fp64 oracle on identical inputs.
+
+Small shapes are compared element by element over the whole output; they
+span several 64-key tiles and 32-row query blocks and include ragged tails.
+The five measured workloads run at their full sizes in the same launch
+configuration the benchmark times, and are compared on sampled query
+positions (every batch and head of each sampled position), which the oracle
+evaluates exactly.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import inputs
+import oracle
+from inputs.configs import WORKLOADS, make_inputs
+from tests.parity import check
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+from tests import gpu_util  # noqa: E402
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+SMALL = [
+    # B, S, H_q, H_kv, d, causal
+    (1, 1, 1, 1, 128, False), (1, 1, 4, 2, 64, True), (1, 2, 2, 1, 128, True),
+    (1, 31, 4, 4, 128, False), (1, 33, 4, 4, 128, True), (1, 63, 2, 1, 64, False),
+    (1, 64, 8, 2, 128, True), (1, 65, 8, 2, 128, False), (2, 127, 4, 4, 64, True),
+    (1, 129, 16, 1, 128, True), (1, 257, 6, 2, 128, False), (3, 200, 6, 3, 64, True),
+    (1, 1000, 8, 8, 128, True), (1, 1000, 8, 2, 128, False), (2, 513, 16, 4, 64, False),
+    (1, 777, 4, 1, 32, True), (2, 96, 2, 2, 32, False), (1, 2048, 16, 16, 128, True),
+    (1, 1500, 12, 4, 128, True), (1, 300, 32, 2, 64, True),
+]
+
+
+@pytest.mark.parametrize("B,S,H_q,H_kv,d,causal", SMALL)
+def test_small_shapes_full_output(B, S, H_q, H_kv, d, causal):
+    _say(f"small B={B} S={S} H_q={H_q} H_kv={H_kv} d={d} causal={causal}")
+    seed = 1000 + S * 131 + H_q * 7 + H_kv + d + causal
+    q = inputs.normal(seed, 0, (B, S, H_q, d), "bf16", 0.5)
+    k = inputs.normal(seed, 1, (B, S, H_kv, d), "bf16", 0.5)
+    v = inputs.normal(seed, 2, (B, S, H_kv, d), "bf16", 0.5)
+    scale = 1.0 / math.sqrt(d)
+    got = gpu_util.to_host_f64(gpu_util.run(q, k, v, scale, causal))
+    ref = oracle.attention(q, k, v, float(np.float32(scale)), causal=causal)
+    check(got, ref, "bf16", f"S={S} H={H_q}/{H_kv} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 0.5, 1e-3])
+def test_scale_values(scale):
+    _say(f"scale {scale}")
+    B, S, H_q, H_kv, d = 1, 200, 4, 2, 128
+    q = inputs.normal(55, 0, (B, S, H_q, d), "bf16", 0.5)
+    k = inputs.normal(55, 1, (B, S, H_kv, d), "bf16", 0.5)
+    v = inputs.normal(55, 2, (B, S, H_kv, d), "bf16", 0.5)
+    for causal in (False, True):
+        got = gpu_util.to_host_f64(gpu_util.run(q, k, v, scale, causal))
+        ref = oracle.attention(q, k, v, float(np.float32(scale)), causal=causal)
+        check(got, ref, "bf16", f"scale={scale} causal={causal}")
+
+
+def test_tiny_f32_workload_full():
+    w = WORKLOADS["tiny_f32"]
+    _say("workload tiny_f32")
+    q, k, v, _ = make_inputs(w, "gqa")
+    got = gpu_util.to_host_f64(gpu_util.run(q, k, v, w.scale, w.causal))
+    ref = oracle.attention(q, k, v, float(np.float32(w.scale)), causal=w.causal)
+    check(got, ref, "f32", "tiny_f32")
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_f32_other_head_dims(d):
+    _say(f"f32 d={d}")
+    q = inputs.normal(66, 0, (2, 130, 6, d), "f32")
+    k = inputs.normal(66, 1, (2, 130, 3, d), "f32")
+    v = inputs.normal(66, 2, (2, 130, 3, d), "f32")
+    for causal in (False, True):
+        got = gpu_util.to_host_f64(gpu_util.run(q, k, v, 1 / math.sqrt(d), causal))
+        ref = oracle.attention(q, k, v, float(np.float32(1 / math.sqrt(d))), causal=causal)
+        check(got, ref, "f32", f"f32 d={d} causal={causal}")
+
+
+def sample_rows(S, seed, extra=()):
+    """Query positions checked at full size: both ends, tile and block
+    boundaries and seeded random positions."""
+    rng = np.random.default_rng(seed)
+    picks = [np.arange(0, min(S, 64)), np.arange(max(0, S - 64), S),
+             rng.integers(0, S, 64)]
+    step = max(64, S // 16)
+    b = np.arange(step, S, step)
+    picks += [b - 1, b]
+    picks.append(np.asarray(extra, dtype=np.int64))
+    rows = np.unique(np.concatenate(picks))
+    return rows[(rows >= 0) & (rows < S)]
+
+
+FULL = [("sweep_s4096", "mha"), ("sweep_s4096", "gqa"), ("sweep_s4096", "sqa"), ("sweep_s4096", "xsqa"),
+        ("encoder_s32k", "sqa"), ("encoder_s32k", "mha"), ("causal_s131k", "sqa"),
+        ("causal_s131k", "mha"), ("ragged_s200k", "sqa"), ("ragged_s200k", "gqa")]
+
+
+@pytest.mark.parametrize("name,variant", FULL)
+def test_workload_full_size_sampled(name, variant):
+    w = WORKLOADS[name]
+    vv = w.variant(variant)
+    _say(f"workload {name}/{variant} B={w.B} S={w.S} H={vv.H_q}/{vv.H_kv} d={w.d} causal={w.causal}")
+    q, k, v, peaked = make_inputs(w, variant)
+    extra = []
+    for s in peaked[:16]:
+        extra += [s, s + 1, s + 2, s + 3]
+    rows = sample_rows(w.S, w.seed(variant), extra)
+    o = gpu_util.run(q, k, v, w.scale, w.causal)
+    got = gpu_util.to_host_f64(o[:, torch.from_numpy(rows).to(o.device)])
+    del o
+    ref = oracle.attention(q, k, v, float(np.float32(w.scale)), causal=w.causal, rows=rows)
+    st = check(got, ref, "bf16", f"{name}/{variant}")
+    _say(f"  rows={rows.size} stats={st}")
