@@ -8,9 +8,11 @@
 // the query-head count free as in Sparse Query Attention ("Sparse Query
 // Attention (SQA)", abstract).  The softmax is evaluated online over key
 // tiles (running row maximum and row sum), which equals the row-normalised
-// form D(A)^-1 A V exactly in real arithmetic.
+// form D(A)^-1 A V of the quantum-attention review's classical baseline
+// exactly in real arithmetic.
 //
-// bf16 kernel design (one workgroup = WAVES waves of 64 lanes):
+// bf16 kernel design (one workgroup = WAVES waves of 64 lanes, WAVES = 8 for
+// large grids, 4 otherwise):
 //  * A workgroup owns one key/value group (b, g) and WAVES "items"; an item
 //    is 32 consecutive query positions of one query head of that group.
 //    Items are ordered position-block-major, head-minor, so the waves of a
@@ -28,7 +30,9 @@
 //  * K and V tiles of 64 keys go global -> LDS directly
 //    (global_load_lds_dwordx4), double-buffered, one barrier per tile.  The
 //    LDS layout XOR-swizzles 16-byte chunks by the row bits so that both the
-//    K operand reads and the transposed V reads are bank-conflict free.
+//    K operand reads and the transposed V reads are bank-conflict free.  LDS
+//    operand reads run several MFMAs ahead of their use.
+//  * Online softmax in the exp2 domain with a lazily moved running maximum.
 //  * Causal: tiles above a wave's last row are skipped, diagonal tiles are
 //    masked per element; sequence tails: key rows are clamped for the loads
 //    and masked in the scores, query rows past S are never stored.
@@ -44,11 +48,11 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 #define SQA_LDS __attribute__((address_space(3)))
 
 constexpr int kKeys = 64;         // keys per K/V tile
 constexpr int kRows = 32;         // query positions per item (one wave)
+constexpr float kLazyLog2 = 8.0f;  // running-max slack before a rescale (log2 units)
 
 struct Bf16Params {
   const uint16_t* q;
@@ -100,28 +104,77 @@ __device__ __forceinline__ float wave_pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Stage one [kKeys][D] tile of K or V for group (b, g) into LDS.  Each wave
-// issues kKeys*D/8/64/WAVES global->LDS copies of 16 bytes per lane; lane i of
-// copy u fills LDS chunk u*64+i, so the global chunk it fetches is the one
-// the swizzle places there.  Rows at or past S are clamped to S-1 (in
-// bounds); their scores are masked and their probabilities are exactly 0.
-template <int D, int WAVES>
-__device__ __forceinline__ void stage_tile(const uint16_t* head_base, int64_t row_stride, int kv0,
-                                           int S, SQA_LDS uint16_t* tile, int wave, int lane) {
-  constexpr int CH = D / 8;
-  constexpr int COPIES = kKeys * CH / 64;
-  static_assert(COPIES % WAVES == 0, "tile copies must split evenly over the waves");
-#pragma unroll
-  for (int u0 = 0; u0 < COPIES; u0 += WAVES) {
-    const int u = u0 + wave;
-    const int pc = u * 64 + lane;
-    const int row = pc / CH;
-    const int chunk = (pc % CH) ^ swz<D>(row);
-    const int grow = min(kv0 + row, S - 1);
-    const uint16_t* src = head_base + (int64_t)grow * row_stride + chunk * 8;
-    __builtin_amdgcn_global_load_lds((const void*)src, (SQA_LDS void*)(tile + u * 512), 16, 0, 0);
-  }
+// Global -> LDS copy of 16 bytes per lane: lane i reads sbase + voff and
+// writes LDS at lds + 16*i.  Issued from inline asm so that the compiler's
+// wait-count bookkeeping does not treat every later LDS read as dependent on
+// it (the caller waits for these copies explicitly with vmcnt before the
+// barrier that publishes the tile).  No output registers; M0 is set here and
+// is not used by any compiler-generated code in these kernels.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds) : "memory");
 }
+
+// Wait until this wave's outstanding global -> LDS copies have landed.
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const SQA_LDS void* p) { return (uint32_t)(uintptr_t)p; }
+
+// Scheduling pattern for an MFMA chain fed from LDS: READS loads per MFMA,
+// issued AHEAD MFMAs before their use.
+template <int N, int READS, int AHEAD>
+__device__ __forceinline__ void lds_mfma_pipeline_hint() {
+  __builtin_amdgcn_sched_group_barrier(0x100, READS * AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+}
+
+// Stage one [kKeys][D] tile of K or V into LDS with global->LDS copies of 16
+// bytes per lane.  Copy u (u = j*WAVES + wave) fills LDS chunks u*64 ...
+// u*64+63, so lane i of copy u fetches the global chunk the swizzle places at
+// LDS chunk u*64+i.  `lane_off[j]` is that chunk's element offset from the
+// tile's first row; it does not depend on the tile.  In the tail tile, rows at
+// or past S are clamped to S-1 (in bounds; their scores are masked and their
+// probabilities are exactly 0).
+template <int D, int WAVES>
+struct TileCopy {
+  static constexpr int CH = D / 8;
+  static constexpr int COPIES = kKeys * CH / 64;
+  static constexpr int PER_WAVE = COPIES / WAVES;
+  static_assert(COPIES % WAVES == 0, "tile copies must split evenly over the waves");
+  int lane_off[PER_WAVE];
+  int row[PER_WAVE];
+  int chunk[PER_WAVE];
+
+  __device__ __forceinline__ void init(int64_t row_stride, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int pc = (j * WAVES + wave) * 64 + lane;
+      row[j] = pc / CH;
+      chunk[j] = (pc % CH) ^ swz<D>(row[j]);
+      lane_off[j] = row[j] * (int)row_stride + chunk[j] * 8;
+    }
+  }
+
+  __device__ __forceinline__ void issue(const uint16_t* tile_base, int64_t row_stride, int rows_left,
+                                        SQA_LDS uint16_t* tile, int wave) const {
+    if (rows_left >= kKeys) {
+#pragma unroll
+      for (int j = 0; j < PER_WAVE; ++j)
+        dma16(tile_base, (uint32_t)lane_off[j] * 2u, lds_addr(tile + (j * WAVES + wave) * 512));
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER_WAVE; ++j) {
+        const int r = min(row[j], rows_left - 1);
+        dma16(tile_base, (uint32_t)(r * (int)row_stride + chunk[j] * 8) * 2u, lds_addr(tile + (j * WAVES + wave) * 512));
+      }
+    }
+  }
+};
 
 template <int D, bool CAUSAL, int WAVES>
 __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_bf16(Bf16Params p) {
@@ -130,7 +183,10 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_bf16(Bf16Params p) {
   constexpr int NB = kKeys / 32;  // 32-key blocks per tile
   constexpr int NT = kKeys / 16;  // 16-key MFMA steps of P.V per tile
   constexpr int TILE = kKeys * D; // elements per tile
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[4 * TILE];  // K0 K1 V0 V1
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v1[TILE];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -159,12 +215,12 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_bf16(Bf16Params p) {
   const int64_t kv_stride = (int64_t)p.H_kv * D;
   const uint16_t* k_base = p.k + ((int64_t)b * S * p.H_kv + g) * D;
   const uint16_t* v_base = p.v + ((int64_t)b * S * p.H_kv + g) * D;
-  SQA_LDS uint16_t* lds_k = (SQA_LDS uint16_t*)lds;
-  SQA_LDS uint16_t* lds_v = (SQA_LDS uint16_t*)lds + 2 * TILE;
 
+  TileCopy<D, WAVES> cp;
+  cp.init(kv_stride, wave, lane);
   // first K/V tile in flight while Q loads
-  stage_tile<D, WAVES>(k_base, kv_stride, 0, S, lds_k, wave, lane);
-  stage_tile<D, WAVES>(v_base, kv_stride, 0, S, lds_v, wave, lane);
+  cp.issue(k_base, kv_stride, S, (SQA_LDS uint16_t*)lds_k0, wave);
+  cp.issue(v_base, kv_stride, S, (SQA_LDS uint16_t*)lds_v0, wave);
 
   // Q^T as the B operand: lane holds query (pos0 + col), head dims
   // ks*16 + half*8 ... +7.
@@ -210,57 +266,66 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_bf16(Bf16Params p) {
   const int my_q = pos0 + col;
   const int wave_last = pos0 + kRows - 1;
 
-  for (int t = 0; t < n_tiles; ++t) {
+  auto step = [&](int t, SQA_LDS uint16_t* kt_cur, SQA_LDS uint16_t* vt_cur, SQA_LDS uint16_t* kt_nxt, SQA_LDS uint16_t* vt_nxt) {
     const int kv0 = t * kKeys;
-    const int buf = t & 1;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile-t copies landed
-    __syncthreads();                      // everyone's copies landed; tile t-1 fully consumed
+    wait_copies();     // this wave's copies of tile t landed
+    __syncthreads();   // everyone's copies landed; tile t-1 fully consumed
     if (t + 1 < n_tiles) {
-      stage_tile<D, WAVES>(k_base, kv_stride, kv0 + kKeys, S, lds_k + (buf ^ 1) * TILE, wave, lane);
-      stage_tile<D, WAVES>(v_base, kv_stride, kv0 + kKeys, S, lds_v + (buf ^ 1) * TILE, wave, lane);
+      const int64_t nxt = (int64_t)(kv0 + kKeys) * kv_stride;
+      cp.issue(k_base + nxt, kv_stride, S - kv0 - kKeys, kt_nxt, wave);
+      cp.issue(v_base + nxt, kv_stride, S - kv0 - kKeys, vt_nxt, wave);
     }
-    if (!active) continue;
-    if (CAUSAL && kv0 > wave_last) continue;   // whole tile above this wave's rows
+    if (!active) return;
+    if (CAUSAL && kv0 > wave_last) return;   // whole tile above this wave's rows
 
-    const SQA_LDS uint16_t* kt = lds_k + buf * TILE;
-    const SQA_LDS uint16_t* vt = lds_v + buf * TILE;
+    const SQA_LDS uint16_t* kt = kt_cur;
+    const SQA_LDS uint16_t* vt = vt_cur;
 
     // S^T = K Q^T
     f32x16 s[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      s[nb] = (f32x16){};
+    for (int nb = 0; nb < NB; ++nb) s[nb] = (f32x16){};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
         const bf16x8 a = *(const SQA_LDS bf16x8*)(kt + nb * 32 * D + k_off[ks]);
         s[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[nb], 0, 0, 0);
       }
-    }
+    lds_mfma_pipeline_hint<KS * NB, 1, 4>();
 
-    // mask: key index of s[nb][r] is kv0 + nb*32 + 8*(r/4) + 4*half + r%4
+    // mask: key index of s[nb][r] is kv0 + 4*half + (nb*32 + 8*(r/4) + r%4)
     const bool need_mask = (kv0 + kKeys > S) || (CAUSAL && kv0 + kKeys - 1 > pos0);
     if (need_mask) {
-      const int lim = CAUSAL ? min(my_q, S - 1) : S - 1;
+      const int lim = (CAUSAL ? min(my_q, S - 1) : S - 1) - kv0 - 4 * half;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key > lim) s[nb][r] = -__builtin_inff();
-        }
+        for (int r = 0; r < 16; ++r)
+          if (nb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[nb][r] = -__builtin_inff();
     }
 
-    // online softmax in the exp2 domain: p = 2^(c*s - m)
+    // online softmax in the exp2 domain: p = 2^(c*s - m).  The running max m
+    // is only moved when a row's maximum grows by more than 2^kLazyLog2, so
+    // p <= 2^kLazyLog2 and the accumulator is rarely rescaled; the result is
+    // the same for any m (it cancels in the final division by the row sum).
     float mx = -__builtin_inff();
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][r]);
     mx = wave_pair_max(mx);
-    const float m_new = fmaxf(m_run, mx * c);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    const float neg_m = -m_new;
+    const float m_cand = mx * c;
+    const bool grow = m_cand > m_run + kLazyLog2;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? m_cand : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    }
+    const float neg_m = -m_run;
     float psum = 0.f;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -270,11 +335,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_bf16(Bf16Params p) {
         s[nb][r] = pv;
         psum += pv;
       }
-    l_run = l_run * alpha + psum;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-    }
+    l_run += psum;
 
     // O^T += V^T P^T, 16 keys per MFMA.  MFMA k-slot half*8 + e maps to key
     // 16*(step%2) + 4*half + e (e < 4) or + 8 + 4*half + (e-4) of block step/2,
@@ -294,6 +355,11 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_bf16(Bf16Params p) {
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[db], 0, 0, 0);
       }
     }
+    lds_mfma_pipeline_hint<NT * DB, 2, 4>();
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, (SQA_LDS uint16_t*)lds_k0, (SQA_LDS uint16_t*)lds_v0, (SQA_LDS uint16_t*)lds_k1, (SQA_LDS uint16_t*)lds_v1);
+    if (t + 1 < n_tiles) step(t + 1, (SQA_LDS uint16_t*)lds_k1, (SQA_LDS uint16_t*)lds_v1, (SQA_LDS uint16_t*)lds_k0, (SQA_LDS uint16_t*)lds_v0);
   }
 
   if (!active) return;
@@ -357,10 +423,10 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
   for (int e = 0; e < D; ++e) op[e] = acc[e] * inv;
 }
 
-constexpr int kWaves = 4;
 
-template <int D, bool CAUSAL>
-hipError_t launch_bf16_t(const LaunchArgs& a) {
+
+template <int D, bool CAUSAL, int WAVES>
+hipError_t launch_bf16_w(const LaunchArgs& a) {
   Bf16Params p;
   p.q = (const uint16_t*)a.q;
   p.k = (const uint16_t*)a.k;
@@ -373,13 +439,25 @@ hipError_t launch_bf16_t(const LaunchArgs& a) {
   p.n_groups = (int)(a.B * a.H_kv);
   const int n_pos_blocks = (int)((a.S + kRows - 1) / kRows);
   p.n_items = p.R * n_pos_blocks;
-  p.chunks = (p.n_items + kWaves - 1) / kWaves;
+  p.chunks = (p.n_items + WAVES - 1) / WAVES;
   p.c = a.c;
   p.q_sign = a.negate_q ? 0x8000u : 0u;
   const int64_t grid = (int64_t)p.n_groups * p.chunks;
-  hipLaunchKernelGGL((attn_fwd_bf16<D, CAUSAL, kWaves>), dim3((unsigned)grid), dim3(kWaves * 64), 0,
+  hipLaunchKernelGGL((attn_fwd_bf16<D, CAUSAL, WAVES>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
                      (hipStream_t)a.stream, p);
   return hipGetLastError();
+}
+
+constexpr int kCUs = 256;
+
+template <int D, bool CAUSAL>
+hipError_t launch_bf16_t(const LaunchArgs& a) {
+  if constexpr (D >= 64) {
+    const int64_t items = (int64_t)(a.H_q / a.H_kv) * ((a.S + kRows - 1) / kRows);
+    const int64_t wgs8 = a.B * a.H_kv * ((items + 7) / 8);
+    if (wgs8 >= 2 * kCUs) return launch_bf16_w<D, CAUSAL, 8>(a);
+  }
+  return launch_bf16_w<D, CAUSAL, 4>(a);
 }
 
 template <int D>
@@ -399,7 +477,7 @@ hipError_t launch_f32_t(const LaunchArgs& a) {
 int64_t bf16_grid_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv) {
   const int64_t R = H_q / H_kv;
   const int64_t items = R * ((S + kRows - 1) / kRows);
-  return B * H_kv * ((items + kWaves - 1) / kWaves);
+  return B * H_kv * ((items + 3) / 4);
 }
 
 hipError_t launch_attn_fwd(const LaunchArgs& a) {
