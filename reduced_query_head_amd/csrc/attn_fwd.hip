@@ -11,8 +11,9 @@
 // form D(A)^-1 A V of the quantum-attention review's classical baseline
 // exactly in real arithmetic.
 //
-// bf16 kernel design (one workgroup = WAVES waves of 64 lanes, WAVES = 8 for
-// large grids, 4 otherwise):
+// bf16 kernel design (one workgroup = WAVES waves of 64 lanes and KEYS-key
+// K/V tiles: WAVES = 8 with 128-key tiles for large grids, 4 with 64-key
+// tiles otherwise):
 //  * A workgroup owns one key/value group (b, g) and WAVES "items"; an item
 //    is 32 consecutive query positions of one query head of that group.
 //    Items are ordered position-block-major, head-minor, so the waves of a
@@ -27,12 +28,13 @@
 //    that holds P[query][key] for 8 keys is exactly the lane the MFMA wants,
 //    once the MFMA's K index is mapped to the keys in the order the score
 //    accumulator holds them.  V^T comes from LDS with ds_read_b64_tr_b16.
-//  * K and V tiles of 64 keys go global -> LDS directly
+//  * K and V tiles go global -> LDS directly
 //    (global_load_lds_dwordx4), double-buffered, one barrier per tile.  The
 //    LDS layout XOR-swizzles 16-byte chunks by the row bits so that both the
 //    K operand reads and the transposed V reads are bank-conflict free.  LDS
 //    operand reads run several MFMAs ahead of their use.
-//  * Online softmax in the exp2 domain with a lazily moved running maximum.
+//  * Online softmax in the exp2 domain with a lazily moved running maximum;
+//    the row sum adds the bf16 probabilities that enter the P.V product.
 //  * Causal: tiles above a wave's last row are skipped, diagonal tiles are
 //    masked per element; sequence tails: key rows are clamped for the loads
 //    and masked in the scores, query rows past S are never stored.
@@ -46,11 +48,11 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 #define SQA_LDS __attribute__((address_space(3)))
 
-constexpr int kKeys = 64;         // keys per K/V tile
 constexpr int kRows = 32;         // query positions per item (one wave)
 constexpr float kLazyLog2 = 8.0f;  // running-max slack before a rescale (log2 units)
 
@@ -87,7 +89,7 @@ __device__ __forceinline__ int swz(int row) {
   }
 }
 
-// element offset of (row, col) inside a swizzled [kKeys][D] tile
+// element offset of (row, col) inside a swizzled [keys][D] tile
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int col) {
   return row * D + (((col >> 3) ^ swz<D>(row)) << 3) + (col & 7);
@@ -133,17 +135,17 @@ __device__ __forceinline__ void lds_mfma_pipeline_hint() {
   for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 }
 
-// Stage one [kKeys][D] tile of K or V into LDS with global->LDS copies of 16
+// Stage one [KEYS][D] tile of K or V into LDS with global->LDS copies of 16
 // bytes per lane.  Copy u (u = j*WAVES + wave) fills LDS chunks u*64 ...
 // u*64+63, so lane i of copy u fetches the global chunk the swizzle places at
 // LDS chunk u*64+i.  `lane_off[j]` is that chunk's element offset from the
 // tile's first row; it does not depend on the tile.  In the tail tile, rows at
 // or past S are clamped to S-1 (in bounds; their scores are masked and their
 // probabilities are exactly 0).
-template <int D, int WAVES>
+template <int D, int WAVES, int KEYS>
 struct TileCopy {
   static constexpr int CH = D / 8;
-  static constexpr int COPIES = kKeys * CH / 64;
+  static constexpr int COPIES = KEYS * CH / 64;
   static constexpr int PER_WAVE = COPIES / WAVES;
   static_assert(COPIES % WAVES == 0, "tile copies must split evenly over the waves");
   int lane_off[PER_WAVE];
@@ -162,7 +164,7 @@ struct TileCopy {
 
   __device__ __forceinline__ void issue(const uint16_t* tile_base, int64_t row_stride, int rows_left,
                                         SQA_LDS uint16_t* tile, int wave) const {
-    if (rows_left >= kKeys) {
+    if (rows_left >= KEYS) {
 #pragma unroll
       for (int j = 0; j < PER_WAVE; ++j)
         dma16(tile_base, (uint32_t)lane_off[j] * 2u, lds_addr(tile + (j * WAVES + wave) * 512));
@@ -176,13 +178,13 @@ struct TileCopy {
   }
 };
 
-template <int D, bool CAUSAL, int WAVES>
+template <int D, bool CAUSAL, int WAVES, int KEYS>
 __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_bf16(Bf16Params p) {
   constexpr int KS = D / 16;      // MFMA k-steps over the head dimension
   constexpr int DB = D / 32;      // 32-row blocks of O^T
-  constexpr int NB = kKeys / 32;  // 32-key blocks per tile
-  constexpr int NT = kKeys / 16;  // 16-key MFMA steps of P.V per tile
-  constexpr int TILE = kKeys * D; // elements per tile
+  constexpr int NB = KEYS / 32;  // 32-key blocks per tile
+  constexpr int NT = KEYS / 16;  // 16-key MFMA steps of P.V per tile
+  constexpr int TILE = KEYS * D; // elements per tile
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_v0[TILE];
@@ -210,13 +212,13 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_bf16(Bf16Params p) {
 
   const int last_item = min(chunk * WAVES + WAVES - 1, p.n_items - 1);
   const int wg_last_pos = min((last_item / p.R) * kRows + kRows - 1, S - 1);
-  const int n_tiles = CAUSAL ? wg_last_pos / kKeys + 1 : (S + kKeys - 1) / kKeys;
+  const int n_tiles = CAUSAL ? wg_last_pos / KEYS + 1 : (S + KEYS - 1) / KEYS;
 
   const int64_t kv_stride = (int64_t)p.H_kv * D;
   const uint16_t* k_base = p.k + ((int64_t)b * S * p.H_kv + g) * D;
   const uint16_t* v_base = p.v + ((int64_t)b * S * p.H_kv + g) * D;
 
-  TileCopy<D, WAVES> cp;
+  TileCopy<D, WAVES, KEYS> cp;
   cp.init(kv_stride, wave, lane);
   // first K/V tile in flight while Q loads
   cp.issue(k_base, kv_stride, S, (SQA_LDS uint16_t*)lds_k0, wave);
@@ -267,16 +269,22 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_bf16(Bf16Params p) {
   const int wave_last = pos0 + kRows - 1;
 
   auto step = [&](int t, SQA_LDS uint16_t* kt_cur, SQA_LDS uint16_t* vt_cur, SQA_LDS uint16_t* kt_nxt, SQA_LDS uint16_t* vt_nxt) {
-    const int kv0 = t * kKeys;
+    const int kv0 = t * KEYS;
     wait_copies();     // this wave's copies of tile t landed
     __syncthreads();   // everyone's copies landed; tile t-1 fully consumed
-    if (t + 1 < n_tiles) {
-      const int64_t nxt = (int64_t)(kv0 + kKeys) * kv_stride;
-      cp.issue(k_base + nxt, kv_stride, S - kv0 - kKeys, kt_nxt, wave);
-      cp.issue(v_base + nxt, kv_stride, S - kv0 - kKeys, vt_nxt, wave);
+    // copies of tile t+1 into the other buffers; issued after this tile's
+    // K.Q^T MFMAs so that their issue overlaps matrix work
+    auto copy_next = [&]() {
+      if (t + 1 < n_tiles) {
+        const int64_t nxt = (int64_t)(kv0 + KEYS) * kv_stride;
+        cp.issue(k_base + nxt, kv_stride, S - kv0 - KEYS, kt_nxt, wave);
+        cp.issue(v_base + nxt, kv_stride, S - kv0 - KEYS, vt_nxt, wave);
+      }
+    };
+    if (!active || (CAUSAL && kv0 > wave_last)) {  // no work on this tile
+      copy_next();
+      return;
     }
-    if (!active) return;
-    if (CAUSAL && kv0 > wave_last) return;   // whole tile above this wave's rows
 
     const SQA_LDS uint16_t* kt = kt_cur;
     const SQA_LDS uint16_t* vt = vt_cur;
@@ -293,9 +301,10 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_bf16(Bf16Params p) {
         s[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[nb], 0, 0, 0);
       }
     lds_mfma_pipeline_hint<KS * NB, 1, 4>();
+    copy_next();
 
     // mask: key index of s[nb][r] is kv0 + 4*half + (nb*32 + 8*(r/4) + r%4)
-    const bool need_mask = (kv0 + kKeys > S) || (CAUSAL && kv0 + kKeys - 1 > pos0);
+    const bool need_mask = (kv0 + KEYS > S) || (CAUSAL && kv0 + KEYS - 1 > pos0);
     if (need_mask) {
       const int lim = (CAUSAL ? min(my_q, S - 1) : S - 1) - kv0 - 4 * half;
 #pragma unroll
@@ -326,25 +335,26 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_bf16(Bf16Params p) {
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
     }
     const float neg_m = -m_run;
-    float psum = 0.f;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][r], c, neg_m));
-        s[nb][r] = pv;
-        psum += pv;
-      }
-    l_run += psum;
+      for (int r = 0; r < 16; ++r) s[nb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][r], c, neg_m));
 
     // O^T += V^T P^T, 16 keys per MFMA.  MFMA k-slot half*8 + e maps to key
     // 16*(step%2) + 4*half + e (e < 4) or + 8 + 4*half + (e-4) of block step/2,
     // which is where the score accumulator left them.
+    // the row sum adds the bf16 probabilities the MFMA multiplies, two per
+    // v_dot2 (fp32 accumulation)
+    float psum = 0.f;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int st = 0; st < NT; ++st) {
       bf16x8 pb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[st >> 1][(st & 1) * 8 + e];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        psum = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){pb[e], pb[e + 1]}, ones, psum, false);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
@@ -356,6 +366,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_bf16(Bf16Params p) {
       }
     }
     lds_mfma_pipeline_hint<NT * DB, 2, 4>();
+    l_run += psum;
   };
   for (int t = 0; t < n_tiles; t += 2) {
     step(t, (SQA_LDS uint16_t*)lds_k0, (SQA_LDS uint16_t*)lds_v0, (SQA_LDS uint16_t*)lds_k1, (SQA_LDS uint16_t*)lds_v1);
@@ -425,7 +436,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
 
 
 
-template <int D, bool CAUSAL, int WAVES>
+template <int D, bool CAUSAL, int WAVES, int KEYS>
 hipError_t launch_bf16_w(const LaunchArgs& a) {
   Bf16Params p;
   p.q = (const uint16_t*)a.q;
@@ -443,7 +454,7 @@ hipError_t launch_bf16_w(const LaunchArgs& a) {
   p.c = a.c;
   p.q_sign = a.negate_q ? 0x8000u : 0u;
   const int64_t grid = (int64_t)p.n_groups * p.chunks;
-  hipLaunchKernelGGL((attn_fwd_bf16<D, CAUSAL, WAVES>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
+  hipLaunchKernelGGL((attn_fwd_bf16<D, CAUSAL, WAVES, KEYS>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
                      (hipStream_t)a.stream, p);
   return hipGetLastError();
 }
@@ -455,9 +466,9 @@ hipError_t launch_bf16_t(const LaunchArgs& a) {
   if constexpr (D >= 64) {
     const int64_t items = (int64_t)(a.H_q / a.H_kv) * ((a.S + kRows - 1) / kRows);
     const int64_t wgs8 = a.B * a.H_kv * ((items + 7) / 8);
-    if (wgs8 >= 2 * kCUs) return launch_bf16_w<D, CAUSAL, 8>(a);
+    if (wgs8 >= 2 * kCUs) return launch_bf16_w<D, CAUSAL, 8, 128>(a);
   }
-  return launch_bf16_w<D, CAUSAL, 4>(a);
+  return launch_bf16_w<D, CAUSAL, 4, 64>(a);
 }
 
 template <int D>
