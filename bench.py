@@ -89,6 +89,28 @@ def time_variant(sqa, torch, w, variant, steps, warmup):
     return res
 
 
+def gemm_context(torch, n=8192, iters=10):
+    """A plain bf16 GEMM from the vendor library on random N(0,1) data, as a
+    practical reference for dense bf16 throughput on this GPU (the chip is
+    power-limited, so random operands run below the nominal peak)."""
+    g = torch.Generator(device="cuda").manual_seed(1)
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    del a, b
+    torch.cuda.empty_cache()
+    return {"op": f"torch.matmul bf16 {n}x{n}x{n}, random N(0,1)", "tflops": round(2 * n ** 3 / ms / 1e9, 1)}
+
+
 def cpu_baseline(w, variant, budget_s):
     """The fp64 oracle, unchanged, on a bounded sample of query positions of
     the same workload (all batches and heads of each sampled position)."""
@@ -175,6 +197,7 @@ def main():
                 "kernel": f"attn_fwd_bf16<d={w.d},causal={int(w.causal)}>",
                 "flops_per_launch": main_res["flops"], "avg_launch_ms": round(main_res["avg_launch_ms"], 4)}
     cpu = cpu_baseline(w, args.variant, args.cpu_budget) if args.cpu_budget > 0 else None
+    gemm = gemm_context(torch) if args.cpu_budget > 0 else None
     v = w.variant(args.variant)
     line = {
         "metric": "attn-fwd TFLOP/s (% bf16 MFMA peak) + tokens/s at 32k-200k, SQA vs MHA/GQA",
@@ -201,6 +224,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "pages_claim": "SQA abstract: up to 3x throughput on 32k-200k sequences; hardware not named",
+        "context_library_gemm": gemm,
     }
     print(json.dumps(line), flush=True)
 
