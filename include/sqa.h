@@ -87,6 +87,26 @@ sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, void* out, 
                         int64_t S, int32_t H_q, int32_t H_kv, int32_t d, sqa_dtype dtype,
                         float scale, int causal, sqa_stream_t stream);
 
+/*
+ * Attention forward that also returns the row log-normaliser
+ *
+ *   lse[b, i, h] = ln( sum_j exp(scale * <q[b,i,h,:], k[b,j,g,:]>) )
+ *
+ * over the same visible keys j: the logarithm of the row sum D_ii of
+ * A = exp(scores) in the row-normalised form D(A)^-1 A V ("Beyond Classical
+ * Attention: Quantum Attention" review, proposed-method section).  With it the
+ * probabilities can be rebuilt as exp(score - lse) without a second pass over
+ * the keys (what a backward pass needs).
+ *
+ *   lse  [B, S, H_q] fp32, device pointer, 4-byte aligned, must not overlap
+ *        q, k, v or out; may be NULL (then this is sqa_attn_fwd).
+ * All other arguments, the layout, ownership and error behaviour are those
+ * of sqa_attn_fwd.
+ */
+sqa_status sqa_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse,
+                            int64_t B, int64_t S, int32_t H_q, int32_t H_kv, int32_t d,
+                            sqa_dtype dtype, float scale, int causal, sqa_stream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* sqa_status_string(sqa_status status);
 

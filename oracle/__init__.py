@@ -35,6 +35,9 @@ def _load():
         lib.sqa_oracle_fwd.restype = ctypes.c_int
         lib.sqa_oracle_fwd.argtypes = [vp, vp, vp, ctypes.c_int, vp, i64, i64, i32, i32, i32,
                                        ctypes.c_double, ctypes.c_int, vp, i64, ctypes.c_int, vp]
+        lib.sqa_oracle_lse.restype = ctypes.c_int
+        lib.sqa_oracle_lse.argtypes = [vp, vp, ctypes.c_int, vp, i64, i64, i32, i32, i32, ctypes.c_double,
+                                       ctypes.c_int, vp, i64, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -78,3 +81,30 @@ def attention(q, k, v, scale, causal=False, rows=None, n_threads=0, return_pairs
     if rc != 0:
         raise MemoryError("oracle: allocation failed")
     return (out, pairs.value) if return_pairs else out
+
+
+def lse(q, k, scale, causal=False, rows=None, n_threads=0):
+    """fp64 log of the softmax normaliser per (b, row, head): [B, n_rows, H_q]."""
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    if q.dtype != k.dtype or q.dtype not in _DTYPE_CODE:
+        raise TypeError("q, k must share one dtype among uint16(bf16 bits), float32, float64")
+    B, S, H_q, d = q.shape
+    if k.shape[:2] != (B, S) or k.shape[3] != d:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape}")
+    H_kv = k.shape[2]
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n_out, rows_ptr = rows.size, ctypes.c_void_p(rows.ctypes.data)
+    else:
+        n_out, rows_ptr = S, None
+    out = np.zeros((B, n_out, H_q), dtype=np.float64)
+    rc = _load().sqa_oracle_lse(ctypes.c_void_p(q.ctypes.data), ctypes.c_void_p(k.ctypes.data),
+                                _DTYPE_CODE[q.dtype], ctypes.c_void_p(out.ctypes.data), B, S, H_q, H_kv, d,
+                                float(scale), 1 if causal else 0, rows_ptr, n_out if rows is not None else 0,
+                                int(n_threads))
+    if rc == -1:
+        raise ValueError("oracle: invalid arguments")
+    if rc != 0:
+        raise MemoryError("oracle: allocation failed")
+    return out

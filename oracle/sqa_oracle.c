@@ -138,3 +138,69 @@ int sqa_oracle_fwd(const void* q, const void* k, const void* v, int dtype, doubl
   if (pairs_out) *pairs_out = pairs;
   return 0;
 }
+
+/*
+ * Row log-normaliser of the same attention: lse[b, r, h] = log D_ii, where
+ * D_ii = sum_j exp(s_j) is the row sum of A = exp(scores) in the D(A)^-1 A V
+ * form (quantum-attention review, proposed-method section) and s_j =
+ * scale * <q_i, k_j> over the visible keys j.  Computed as m + log(sum_j
+ * exp(s_j - m)) with the row maximum m (exact in real arithmetic).  This is
+ * the statistic a backward pass needs to rebuild the probabilities; the pages
+ * do not name it, it is log of the normaliser they write.
+ *
+ * lse_out: fp64, [B, n_out, H_q] with n_out / rows as for sqa_oracle_fwd.
+ */
+int sqa_oracle_lse(const void* q, const void* k, int dtype, double* lse_out, int64_t B, int64_t S,
+                   int32_t H_q, int32_t H_kv, int32_t d, double scale, int causal, const int64_t* rows,
+                   int64_t n_rows, int n_threads) {
+  if (B < 0 || S < 0 || H_q < 1 || H_kv < 1 || d < 1) return -1;
+  if (H_q % H_kv != 0) return -1;
+  if (dtype < 0 || dtype > 2) return -1;
+  if (causal != 0 && causal != 1) return -1;
+  const int64_t n_out = rows ? n_rows : S;
+  if (n_out < 0) return -1;
+  if (rows)
+    for (int64_t r = 0; r < n_rows; ++r)
+      if (rows[r] < 0 || rows[r] >= S) return -1;
+  const int64_t items = B * n_out * (int64_t)H_q;
+  if (items == 0) return 0;
+  const int32_t R = H_q / H_kv;
+  int failed = 0;
+#ifdef _OPENMP
+  if (n_threads <= 0) n_threads = omp_get_max_threads();
+#else
+  n_threads = 1;
+#endif
+#pragma omp parallel num_threads(n_threads)
+  {
+    double* p = (double*)malloc((size_t)(S > 0 ? S : 1) * sizeof(double));
+    if (!p) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < items; ++t) {
+      if (!p) continue;
+      const int64_t b = t / (n_out * H_q);
+      const int64_t r = (t / H_q) % n_out;
+      const int32_t h = (int32_t)(t % H_q);
+      const int64_t i = rows ? rows[r] : r;
+      const int32_t g = h / R;
+      const int64_t last = causal ? i : S - 1;
+      const int64_t q_off = ((b * S + i) * H_q + h) * (int64_t)d;
+      double m = -INFINITY;
+      for (int64_t j = 0; j <= last; ++j) {
+        const int64_t k_off = ((b * S + j) * H_kv + g) * (int64_t)d;
+        double dot = 0.0;
+        for (int32_t e = 0; e < d; ++e) dot += load_elem(q, dtype, q_off + e) * load_elem(k, dtype, k_off + e);
+        p[j] = scale * dot;
+        if (p[j] > m) m = p[j];
+      }
+      double l = 0.0;
+      for (int64_t j = 0; j <= last; ++j) l += exp(p[j] - m);
+      lse_out[(b * n_out + r) * H_q + h] = m + log(l);
+    }
+    free(p);
+  }
+  return failed ? -2 : 0;
+}

@@ -36,6 +36,9 @@ def load_library(path=None):
     lib.sqa_attn_fwd.restype = ctypes.c_int
     lib.sqa_attn_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, ctypes.c_int, ctypes.c_float,
                                  ctypes.c_int, vp]
+    lib.sqa_attn_fwd_lse.restype = ctypes.c_int
+    lib.sqa_attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ctypes.c_int, ctypes.c_float,
+                                     ctypes.c_int, vp]
     lib.sqa_status_string.restype = ctypes.c_char_p
     lib.sqa_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -52,12 +55,20 @@ def attn_fwd_raw(q, k, v, out, B, S, H_q, H_kv, d, dtype, scale, causal, stream)
                                        stream)
 
 
-def attn_fwd(q, k, v, out=None, scale=None, causal=False, stream=None):
+def attn_fwd_lse_raw(q, k, v, out, lse, B, S, H_q, H_kv, d, dtype, scale, causal, stream):
+    """Direct call of sqa_attn_fwd_lse with integer device addresses; returns the status."""
+    return load_library().sqa_attn_fwd_lse(q, k, v, out, lse, B, S, H_q, H_kv, d, dtype, scale, int(causal),
+                                           stream)
+
+
+def attn_fwd(q, k, v, out=None, scale=None, causal=False, stream=None, return_lse=False, lse=None):
     """out[b,i,h] = softmax_j(scale * q[b,i,h].k[b,j,h//R]) . v[b,j,h//R].
 
     q: [B, S, H_q, d], k and v: [B, S, H_kv, d], torch tensors on the GPU,
     contiguous, all bfloat16 or all float32.  scale defaults to 1/sqrt(d).
     The kernel is enqueued on `stream` (default: torch's current stream).
+    With return_lse (or an `lse` tensor given) also returns the fp32
+    [B, S, H_q] row log-normaliser ln(sum_j exp(scale * q.k_j)).
     """
     import torch
 
@@ -85,6 +96,16 @@ def attn_fwd(q, k, v, out=None, scale=None, causal=False, stream=None):
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    if return_lse or lse is not None:
+        if lse is None:
+            lse = torch.empty((B, S, H_q), dtype=torch.float32, device=q.device)
+        elif lse.shape != (B, S, H_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 tensor of shape [B, S, H_q]")
+        st = attn_fwd_lse_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, S,
+                              H_q, H_kv, d, dtype, float(scale), causal, handle)
+        if st != SQA_OK:
+            raise SqaError(st, status_string(st))
+        return out, lse
     st = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, S, H_q, H_kv, d,
                       dtype, float(scale), causal, handle)
     if st != SQA_OK:

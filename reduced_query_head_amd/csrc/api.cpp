@@ -34,9 +34,9 @@ SQA_API const char* sqa_status_string(sqa_status status) {
   return "unknown status";
 }
 
-SQA_API sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, void* out, int64_t B,
-                                int64_t S, int32_t H_q, int32_t H_kv, int32_t d, sqa_dtype dtype,
-                                float scale, int causal, sqa_stream_t stream) {
+SQA_API sqa_status sqa_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse,
+                                    int64_t B, int64_t S, int32_t H_q, int32_t H_kv, int32_t d,
+                                    sqa_dtype dtype, float scale, int causal, sqa_stream_t stream) {
   // head counts: groups of H_q / H_kv query heads share one K/V head, so the
   // group count must divide the head count (GQA module's assertion)
   if (B < 0 || S < 0 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0) return SQA_ERR_INVALID_ARGUMENT;
@@ -57,6 +57,14 @@ SQA_API sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, voi
   if (ranges_overlap(out, q_bytes, q, q_bytes) || ranges_overlap(out, q_bytes, k, kv_bytes) ||
       ranges_overlap(out, q_bytes, v, kv_bytes))
     return SQA_ERR_INVALID_ARGUMENT;
+  if (lse) {
+    int64_t lse_bytes;
+    if (!mul_ok(rows, (int64_t)H_q * 4, &lse_bytes)) return SQA_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)lse & 3u) || ranges_overlap(lse, lse_bytes, q, q_bytes) ||
+        ranges_overlap(lse, lse_bytes, k, kv_bytes) || ranges_overlap(lse, lse_bytes, v, kv_bytes) ||
+        ranges_overlap(lse, lse_bytes, out, q_bytes))
+      return SQA_ERR_INVALID_ARGUMENT;
+  }
 
   if (d != 32 && d != 64 && d != 128) return SQA_ERR_UNSUPPORTED;
   // kernels index positions with 32-bit integers
@@ -72,6 +80,7 @@ SQA_API sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, voi
   a.k = k;
   a.v = v;
   a.out = out;
+  a.lse = lse;
   a.B = B;
   a.S = S;
   a.H_q = H_q;
@@ -88,4 +97,10 @@ SQA_API sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, voi
   a.causal = causal;
   a.stream = (void*)stream;
   return sqa::launch_attn_fwd(a) == hipSuccess ? SQA_OK : SQA_ERR_HIP;
+}
+
+SQA_API sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, void* out, int64_t B,
+                                int64_t S, int32_t H_q, int32_t H_kv, int32_t d, sqa_dtype dtype,
+                                float scale, int causal, sqa_stream_t stream) {
+  return sqa_attn_fwd_lse(q, k, v, out, nullptr, B, S, H_q, H_kv, d, dtype, scale, causal, stream);
 }

@@ -70,6 +70,7 @@ struct Bf16Params {
   int chunks;            // ceil(n_items / WAVES), workgroups per group
   float c;               // |scale| * log2(e), strictly positive
   uint32_t q_sign;       // 0x8000 when scale < 0: q is negated on load (exact)
+  float* lse;            // optional [B, S, H_q] row log-normaliser (natural log)
 };
 
 // 16-byte chunk swizzle inside a tile row.  XOR-linear in the low row bits;
@@ -376,7 +377,11 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_bf16(Bf16Params p) {
   if (!active) return;
   const int out_pos = pos0 + col;
   if (out_pos >= S) return;  // lanes l and l^32 share out_pos, so pairs leave together
-  const float inv = 1.0f / wave_pair_sum(l_run);
+  const float l_tot = wave_pair_sum(l_run);
+  const float inv = 1.0f / l_tot;
+  // log of the row normaliser: scores entered the softmax as s*c with
+  // c = scale*log2(e), so ln(sum_j exp(scale*s_j)) = ln2 * (m + log2(l))
+  if (p.lse && half == 0) p.lse[((int64_t)b * S + out_pos) * p.H_q + h] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
   uint16_t* op = p.o + (((int64_t)b * S + out_pos) * p.H_q + h) * D;
   // O^T[db] register r holds head dim db*32 + 8*(r/4) + 4*half + r%4
 #pragma unroll
@@ -396,8 +401,8 @@ template <int D>
 __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
                                                     const float* __restrict__ k,
                                                     const float* __restrict__ v, float* __restrict__ o,
-                                                    int64_t B, int S, int H_q, int H_kv, int R, float c,
-                                                    int causal) {
+                                                    float* __restrict__ lse, int64_t B, int S, int H_q,
+                                                    int H_kv, int R, float c, int causal) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= B * S * H_q) return;
   const int h = (int)(t % H_q);
@@ -429,6 +434,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
     for (int e = 0; e < D; ++e) acc[e] = __builtin_fmaf(pj, vp[e], acc[e] * alpha);
   }
   const float inv = 1.0f / l;
+  if (lse) lse[t] = (m + log2f(l)) * 0.69314718055994531f;
   float* op = o + t * D;
 #pragma unroll
   for (int e = 0; e < D; ++e) op[e] = acc[e] * inv;
@@ -453,6 +459,7 @@ hipError_t launch_bf16_w(const LaunchArgs& a) {
   p.chunks = (p.n_items + WAVES - 1) / WAVES;
   p.c = a.c;
   p.q_sign = a.negate_q ? 0x8000u : 0u;
+  p.lse = a.lse;
   const int64_t grid = (int64_t)p.n_groups * p.chunks;
   hipLaunchKernelGGL((attn_fwd_bf16<D, CAUSAL, WAVES, KEYS>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
                      (hipStream_t)a.stream, p);
@@ -478,7 +485,7 @@ hipError_t launch_f32_t(const LaunchArgs& a) {
   // fp32 kernel keeps the sign of scale in c (no bf16 operand to negate)
   const float c = a.negate_q ? -a.c : a.c;
   hipLaunchKernelGGL((attn_fwd_f32<D>), dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)a.stream,
-                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out, a.B,
+                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out, a.lse, a.B,
                      (int)a.S, a.H_q, a.H_kv, a.H_q / a.H_kv, c, a.causal);
   return hipGetLastError();
 }

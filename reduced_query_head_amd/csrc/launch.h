@@ -12,6 +12,7 @@ struct LaunchArgs {
   const void* k;
   const void* v;
   void* out;
+  float* lse;      // optional row log-normaliser output, [B, S, H_q]
   int64_t B;
   int64_t S;
   int32_t H_q;

@@ -69,3 +69,25 @@ def test_sequence_too_long_is_unsupported():
 def test_empty_is_noop():
     assert _call(B=0, q=0, k=0, v=0, out=0) == sqa.SQA_OK
     assert _call(S=0, q=0, k=0, v=0, out=0) == sqa.SQA_OK
+
+
+def _call_lse(lse, **kw):
+    args = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), out=FAKE + (3 << 30), B=1, S=128, H_q=8,
+                H_kv=2, d=128, dtype=0, scale=0.088, causal=0)
+    args.update(kw)
+    a = args
+    return sqa.attn_fwd_lse_raw(a["q"], a["k"], a["v"], a["out"], lse, a["B"], a["S"], a["H_q"], a["H_kv"],
+                                a["d"], a["dtype"], a["scale"], a["causal"], 0)
+
+
+@pytest.mark.parametrize("lse", [FAKE + (4 << 30) + 2,        # misaligned
+                                 FAKE + (3 << 30) + 4096,     # inside out
+                                 FAKE + 64])                  # inside q
+def test_lse_invalid(lse):
+    assert _call_lse(lse) == sqa.SQA_ERR_INVALID_ARGUMENT
+
+
+def test_lse_rejects_the_same_errors_as_forward():
+    assert _call_lse(FAKE + (4 << 30), H_q=6, H_kv=4) == sqa.SQA_ERR_INVALID_ARGUMENT
+    assert _call_lse(FAKE + (4 << 30), d=96) == sqa.SQA_ERR_UNSUPPORTED
+    assert _call_lse(0, B=0, q=0, k=0, v=0, out=0) == sqa.SQA_OK

@@ -17,6 +17,7 @@ import inputs
 import oracle
 from inputs.configs import WORKLOADS, make_inputs
 from tests.parity import check
+import reduced_query_head_amd as sqa
 
 pytestmark = pytest.mark.gpu
 
@@ -125,3 +126,72 @@ def test_workload_full_size_sampled(name, variant):
     ref = oracle.attention(q, k, v, float(np.float32(w.scale)), causal=w.causal, rows=rows)
     st = check(got, ref, "bf16", f"{name}/{variant}")
     _say(f"  rows={rows.size} stats={st}")
+
+
+# Row log-normaliser.  The GPU forms l as the sum of the bf16-rounded
+# probabilities that enter the P.V product.  Each term carries a relative
+# rounding error of at most 2^-9 and all terms are positive, so the sum is off
+# by at most 2^-9 relative and |d ln l| <= 2^-9 ~ 1.95e-3 for every row (v_exp
+# and v_log add ~1e-7).  Short rows average little (a 2-key row sees nearly the
+# full 2^-9), so the mean bound is 1e-3.  fp32 inputs: exact p, fp32 sums.
+LSE_BOUNDS = {"bf16": (2.5e-3, 1e-3), "f32": (2e-5, 2e-6)}
+
+
+def _check_lse(got, ref, dtype, what):
+    err = np.abs(got.astype(np.float64) - ref)
+    mx, mean = LSE_BOUNDS[dtype]
+    assert np.isfinite(got).all(), what
+    assert err.max() <= mx and err.mean() <= mean, f"{what}: lse max {err.max():.3g} mean {err.mean():.3g}"
+
+
+@pytest.mark.parametrize("B,S,H_q,H_kv,d,causal", [
+    (1, 1, 2, 1, 128, False), (1, 77, 4, 2, 128, True), (2, 300, 8, 8, 64, False), (1, 1000, 8, 2, 128, True),
+    (2, 1100, 64, 8, 128, True), (1, 500, 4, 1, 32, False)])
+def test_lse_small_shapes(B, S, H_q, H_kv, d, causal):
+    _say(f"lse B={B} S={S} H={H_q}/{H_kv} d={d} causal={causal}")
+    seed = 4000 + S + H_q + d
+    q = inputs.normal(seed, 0, (B, S, H_q, d), "bf16", 0.5)
+    k = inputs.normal(seed, 1, (B, S, H_kv, d), "bf16", 0.5)
+    v = inputs.normal(seed, 2, (B, S, H_kv, d), "bf16", 0.5)
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = (gpu_util.to_device(a) for a in (q, k, v))
+    o, lse = sqa.attn_fwd(dq, dk, dv, scale=scale, causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    ref_o = oracle.attention(q, k, v, float(np.float32(scale)), causal=causal)
+    ref_l = oracle.lse(q, k, float(np.float32(scale)), causal=causal)
+    check(gpu_util.to_host_f64(o), ref_o, "bf16", "out with lse")
+    _check_lse(lse.cpu().numpy(), ref_l, "bf16", "lse")
+    # the plain entry point gives the same output bits
+    o2 = sqa.attn_fwd(dq, dk, dv, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+
+
+def test_lse_f32_and_negative_scale():
+    q = inputs.normal(71, 0, (1, 200, 4, 64), "f32")
+    k = inputs.normal(71, 1, (1, 200, 2, 64), "f32")
+    v = inputs.normal(71, 2, (1, 200, 2, 64), "f32")
+    dq, dk, dv = (gpu_util.to_device(a) for a in (q, k, v))
+    for scale in (0.125, -0.3):
+        o, lse = sqa.attn_fwd(dq, dk, dv, scale=scale, causal=True, return_lse=True)
+        torch.cuda.synchronize()
+        _check_lse(lse.cpu().numpy(), oracle.lse(q, k, float(np.float32(scale)), causal=True), "f32", f"f32 lse {scale}")
+    qb = inputs.f32_to_bf16_bits(q)
+    kb = inputs.f32_to_bf16_bits(k)
+    vb = inputs.f32_to_bf16_bits(v)
+    o, lse = sqa.attn_fwd(*(gpu_util.to_device(a) for a in (qb, kb, vb)), scale=-0.3, causal=False, return_lse=True)
+    torch.cuda.synchronize()
+    _check_lse(lse.cpu().numpy(), oracle.lse(qb, kb, float(np.float32(-0.3))), "bf16", "bf16 lse negative scale")
+
+
+@pytest.mark.parametrize("name,variant", [("causal_s131k", "sqa"), ("ragged_s200k", "sqa")])
+def test_lse_full_size_sampled(name, variant):
+    w = WORKLOADS[name]
+    _say(f"lse workload {name}/{variant}")
+    q, k, v, peaked = make_inputs(w, variant)
+    rows = sample_rows(w.S, w.seed(variant) + 1, [s + 1 for s in peaked[:16]])
+    dq, dk, dv = (gpu_util.to_device(a) for a in (q, k, v))
+    o, lse = sqa.attn_fwd(dq, dk, dv, scale=w.scale, causal=w.causal, return_lse=True)
+    got = lse[:, torch.from_numpy(rows).to(lse.device)].cpu().numpy()
+    del o, lse, dq, dk, dv
+    _check_lse(got, oracle.lse(q, k, float(np.float32(w.scale)), causal=w.causal, rows=rows), "bf16", name)

@@ -291,3 +291,55 @@ def test_thread_count_does_not_change_result():
     a = oracle.attention(q, k, v, 0.5, causal=True, n_threads=1)
     b = oracle.attention(q, k, v, 0.5, causal=True, n_threads=4)
     assert np.array_equal(a, b)
+
+
+# ---- row log-normaliser (log-sum-exp of the scaled scores) ------------------
+
+def test_lse_matches_torch_logsumexp():
+    rng = np.random.default_rng(30)
+    B, S, H_q, H_kv, d = 2, 13, 6, 2, 5
+    q, k = _rand(rng, B, S, H_q, d), _rand(rng, B, S, H_kv, d)
+    for causal in (False, True):
+        ours = oracle.lse(q, k, 0.41, causal=causal)
+        kk = np.repeat(k, H_q // H_kv, axis=2)
+        sc = 0.41 * torch.einsum("bihe,bjhe->bhij", torch.from_numpy(q), torch.from_numpy(kk))
+        if causal:
+            sc = sc.masked_fill(torch.ones(S, S, dtype=torch.bool).triu(1), float("-inf"))
+        ref = torch.logsumexp(sc, dim=-1).permute(0, 2, 1).numpy()
+        np.testing.assert_allclose(ours, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_lse_closed_forms():
+    rng = np.random.default_rng(31)
+    # one key: lse = scale * q.k
+    q, k = _rand(rng, 1, 1, 2, 3), _rand(rng, 1, 1, 2, 3)
+    np.testing.assert_allclose(oracle.lse(q, k, 0.7)[0, 0], 0.7 * (q[0, 0] * k[0, 0]).sum(-1), rtol=1e-14)
+    # zero queries: lse = log(number of visible keys)
+    S = 9
+    q0 = np.zeros((1, S, 2, 4))
+    k = _rand(rng, 1, S, 1, 4)
+    np.testing.assert_allclose(oracle.lse(q0, k, 1.0)[0, :, 0], np.full(S, math.log(S)), rtol=1e-15)
+    np.testing.assert_allclose(oracle.lse(q0, k, 1.0, causal=True)[0, :, 0], np.log(np.arange(1, S + 1)), rtol=1e-15)
+
+
+def test_lse_key_shift_adds_q_dot_u():
+    rng = np.random.default_rng(32)
+    q, k = np.abs(_rand(rng, 1, 6, 2, 3)) + 1.0, _rand(rng, 1, 6, 2, 3)
+    u = np.full(3, 250.0)
+    base = oracle.lse(q, k, 0.5)
+    shifted = oracle.lse(q, k + u, 0.5)
+    np.testing.assert_allclose(shifted - base, 0.5 * (q @ u), rtol=1e-12)
+
+
+def test_lse_consistent_with_forward():
+    """exp(s_j - lse) are the weights: sum_j exp(s_j - lse) v_j reproduces the output."""
+    rng = np.random.default_rng(33)
+    B, S, H, d = 1, 7, 2, 3
+    q, k, v = _rand(rng, B, S, H, d), _rand(rng, B, S, H, d), _rand(rng, B, S, H, d)
+    out = oracle.attention(q, k, v, 0.6, causal=True)
+    L = oracle.lse(q, k, 0.6, causal=True)
+    for h in range(H):
+        s = 0.6 * q[0, :, h] @ k[0, :, h].T
+        w = np.tril(np.exp(s - L[0, :, h, None]))
+        np.testing.assert_allclose(w.sum(1), 1.0, rtol=1e-13)
+        np.testing.assert_allclose(w @ v[0, :, h], out[0, :, h], rtol=1e-12, atol=1e-13)
