@@ -38,6 +38,9 @@ def _load():
         lib.sqa_oracle_lse.restype = ctypes.c_int
         lib.sqa_oracle_lse.argtypes = [vp, vp, ctypes.c_int, vp, i64, i64, i32, i32, i32, ctypes.c_double,
                                        ctypes.c_int, vp, i64, ctypes.c_int]
+        lib.sqa_oracle_bwd.restype = ctypes.c_int
+        lib.sqa_oracle_bwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, i64, i64, i32, i32, i32,
+                                       ctypes.c_double, ctypes.c_int, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -108,3 +111,26 @@ def lse(q, k, scale, causal=False, rows=None, n_threads=0):
     if rc != 0:
         raise MemoryError("oracle: allocation failed")
     return out
+
+
+def attention_grad(q, k, v, dout, scale, causal=False, n_threads=0):
+    """fp64 (dq, dk, dv) of the attention for upstream gradient dout (shape of q)."""
+    arrs = [np.ascontiguousarray(a) for a in (q, k, v, dout)]
+    q, k, v, dout = arrs
+    if len({a.dtype for a in arrs}) != 1 or q.dtype not in _DTYPE_CODE:
+        raise TypeError("q, k, v, dout must share one dtype among uint16(bf16 bits), float32, float64")
+    B, S, H_q, d = q.shape
+    if k.shape[:2] != (B, S) or k.shape[3] != d or v.shape != k.shape or dout.shape != q.shape:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape} dout{dout.shape}")
+    H_kv = k.shape[2]
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(k.shape, dtype=np.float64)
+    ptr = lambda a: ctypes.c_void_p(a.ctypes.data)
+    rc = _load().sqa_oracle_bwd(ptr(q), ptr(k), ptr(v), ptr(dout), _DTYPE_CODE[q.dtype], ptr(dq), ptr(dk), ptr(dv),
+                                B, S, H_q, H_kv, d, float(scale), 1 if causal else 0, int(n_threads))
+    if rc == -1:
+        raise ValueError("oracle: invalid arguments")
+    if rc != 0:
+        raise MemoryError("oracle: allocation failed")
+    return dq, dk, dv

@@ -204,3 +204,135 @@ int sqa_oracle_lse(const void* q, const void* k, int dtype, double* lse_out, int
   }
   return failed ? -2 : 0;
 }
+
+/*
+ * Gradient of the same attention with respect to q, k and v, for an upstream
+ * gradient dout = dL/dout.  The pages define only the forward computation;
+ * this is its exact derivative, written out in fp64:
+ *
+ *   p_ij  = exp(s_ij - lse_i)           s_ij = scale * <q_i, k_j>, j visible
+ *   dp_ij = <dout_i, v_j>
+ *   D_i   = sum_j p_ij dp_ij            (= <dout_i, out_i>)
+ *   ds_ij = p_ij (dp_ij - D_i)          (softmax Jacobian)
+ *   dq_i  = scale * sum_j ds_ij k_j
+ *   dk_j  = scale * sum over query heads h of group g, rows i: ds_ij q_i
+ *   dv_j  =         sum over query heads h of group g, rows i: p_ij dout_i
+ *
+ * Key/value heads are shared by the R query heads of their group (GQA
+ * explainer: grouping figure and the expand in the PyTorch module), so their
+ * gradients sum over those heads.  Pass 1 runs per query row (lse_i, D_i,
+ * dq_i); pass 2 per key (dk_j, dv_j), reusing lse_i and D_i.
+ * Outputs are fp64 in BSHD layout: dq [B,S,H_q,d], dk and dv [B,S,H_kv,d].
+ */
+int sqa_oracle_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype, double* dq,
+                   double* dk, double* dv, int64_t B, int64_t S, int32_t H_q, int32_t H_kv, int32_t d,
+                   double scale, int causal, int n_threads) {
+  if (B < 0 || S < 0 || H_q < 1 || H_kv < 1 || d < 1) return -1;
+  if (H_q % H_kv != 0) return -1;
+  if (dtype < 0 || dtype > 2) return -1;
+  if (causal != 0 && causal != 1) return -1;
+  const int64_t rows_q = B * S * (int64_t)H_q;
+  if (rows_q == 0) return 0;
+  const int32_t R = H_q / H_kv;
+  double* lse = (double*)malloc((size_t)rows_q * sizeof(double));
+  double* Dd = (double*)malloc((size_t)rows_q * sizeof(double));
+  if (!lse || !Dd) {
+    free(lse);
+    free(Dd);
+    return -2;
+  }
+  int failed = 0;
+#ifdef _OPENMP
+  if (n_threads <= 0) n_threads = omp_get_max_threads();
+#else
+  n_threads = 1;
+#endif
+
+  /* pass 1: per (b, i, h) row */
+#pragma omp parallel num_threads(n_threads)
+  {
+    double* s = (double*)malloc((size_t)S * sizeof(double));
+    double* dp = (double*)malloc((size_t)S * sizeof(double));
+    if (!s || !dp) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < rows_q; ++t) {
+      if (!s || !dp) continue;
+      const int64_t b = t / ((int64_t)S * H_q);
+      const int64_t i = (t / H_q) % S;
+      const int32_t h = (int32_t)(t % H_q);
+      const int32_t g = h / R;
+      const int64_t last = causal ? i : S - 1;
+      const int64_t qo = ((b * S + i) * H_q + h) * (int64_t)d;
+      double m = -INFINITY;
+      for (int64_t j = 0; j <= last; ++j) {
+        const int64_t ko = ((b * S + j) * H_kv + g) * (int64_t)d;
+        double dot = 0.0, dd = 0.0;
+        for (int32_t e = 0; e < d; ++e) {
+          dot += load_elem(q, dtype, qo + e) * load_elem(k, dtype, ko + e);
+          dd += load_elem(dout, dtype, qo + e) * load_elem(v, dtype, ko + e);
+        }
+        s[j] = scale * dot;
+        dp[j] = dd;
+        if (s[j] > m) m = s[j];
+      }
+      double l = 0.0;
+      for (int64_t j = 0; j <= last; ++j) l += exp(s[j] - m);
+      const double L = m + log(l);
+      double Di = 0.0;
+      for (int64_t j = 0; j <= last; ++j) Di += exp(s[j] - L) * dp[j];
+      lse[t] = L;
+      Dd[t] = Di;
+      double* dqi = dq + qo;
+      for (int32_t e = 0; e < d; ++e) dqi[e] = 0.0;
+      for (int64_t j = 0; j <= last; ++j) {
+        const double ds = exp(s[j] - L) * (dp[j] - Di);
+        const int64_t ko = ((b * S + j) * H_kv + g) * (int64_t)d;
+        for (int32_t e = 0; e < d; ++e) dqi[e] += ds * load_elem(k, dtype, ko + e);
+      }
+      for (int32_t e = 0; e < d; ++e) dqi[e] *= scale;
+    }
+    free(s);
+    free(dp);
+  }
+  if (failed) {
+    free(lse);
+    free(Dd);
+    return -2;
+  }
+
+  /* pass 2: per (b, j, g) key */
+  const int64_t rows_k = B * S * (int64_t)H_kv;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads)
+  for (int64_t t = 0; t < rows_k; ++t) {
+    const int64_t b = t / ((int64_t)S * H_kv);
+    const int64_t j = (t / H_kv) % S;
+    const int32_t g = (int32_t)(t % H_kv);
+    const int64_t ko = ((b * S + j) * H_kv + g) * (int64_t)d;
+    double* dkj = dk + ko;
+    double* dvj = dv + ko;
+    for (int32_t e = 0; e < d; ++e) dkj[e] = dvj[e] = 0.0;
+    for (int32_t h = g * R; h < (g + 1) * R; ++h)
+      for (int64_t i = causal ? j : 0; i < S; ++i) {
+        const int64_t qo = ((b * S + i) * H_q + h) * (int64_t)d;
+        const int64_t row = (b * S + i) * H_q + h;
+        double dot = 0.0, dd = 0.0;
+        for (int32_t e = 0; e < d; ++e) {
+          dot += load_elem(q, dtype, qo + e) * load_elem(k, dtype, ko + e);
+          dd += load_elem(dout, dtype, qo + e) * load_elem(v, dtype, ko + e);
+        }
+        const double p = exp(scale * dot - lse[row]);
+        const double ds = p * (dd - Dd[row]);
+        for (int32_t e = 0; e < d; ++e) {
+          dvj[e] += p * load_elem(dout, dtype, qo + e);
+          dkj[e] += ds * load_elem(q, dtype, qo + e);
+        }
+      }
+    for (int32_t e = 0; e < d; ++e) dkj[e] *= scale;
+  }
+  free(lse);
+  free(Dd);
+  return 0;
+}

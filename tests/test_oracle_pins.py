@@ -343,3 +343,83 @@ def test_lse_consistent_with_forward():
         w = np.tril(np.exp(s - L[0, :, h, None]))
         np.testing.assert_allclose(w.sum(1), 1.0, rtol=1e-13)
         np.testing.assert_allclose(w @ v[0, :, h], out[0, :, h], rtol=1e-12, atol=1e-13)
+
+
+# ---- gradients ---------------------------------------------------------------
+
+def _loss(q, k, v, dout, scale, causal):
+    return float((oracle.attention(q, k, v, scale, causal=causal) * dout).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grad_matches_central_differences_of_the_forward(causal):
+    """dL/dx for L = sum(out * dout), by central differences of the (pinned)
+    forward oracle, element by element."""
+    rng = np.random.default_rng(40)
+    B, S, H_q, H_kv, d = 1, 5, 4, 2, 3
+    q, k, v = _rand(rng, B, S, H_q, d), _rand(rng, B, S, H_kv, d), _rand(rng, B, S, H_kv, d)
+    dout = _rand(rng, B, S, H_q, d)
+    scale = 0.7
+    dq, dk, dv = oracle.attention_grad(q, k, v, dout, scale, causal=causal)
+    eps = 1e-5
+    for arr, grad in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + eps
+            lp = _loss(q, k, v, dout, scale, causal)
+            arr[idx] = old - eps
+            lm = _loss(q, k, v, dout, scale, causal)
+            arr[idx] = old
+            num[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-8)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grad_matches_torch_autograd_fp64(causal):
+    rng = np.random.default_rng(41)
+    B, S, H_q, H_kv, d = 2, 11, 6, 3, 8
+    q, k, v = _rand(rng, B, S, H_q, d), _rand(rng, B, S, H_kv, d), _rand(rng, B, S, H_kv, d)
+    dout = _rand(rng, B, S, H_q, d)
+    dq, dk, dv = oracle.attention_grad(q, k, v, dout, 0.35, causal=causal)
+    R = H_q // H_kv
+    tq = torch.from_numpy(q).requires_grad_()
+    tk = torch.from_numpy(k).requires_grad_()
+    tv = torch.from_numpy(v).requires_grad_()
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq.permute(0, 2, 1, 3), tk.permute(0, 2, 1, 3).repeat_interleave(R, dim=1),
+        tv.permute(0, 2, 1, 3).repeat_interleave(R, dim=1), is_causal=causal, scale=0.35)
+    o.permute(0, 2, 1, 3).backward(torch.from_numpy(dout))
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_grad_sum_invariants():
+    """Softmax rows sum to one, so the key gradients of a group sum to zero and
+    the value gradients sum to the group's summed upstream gradient."""
+    rng = np.random.default_rng(42)
+    B, S, H_q, H_kv, d = 2, 9, 4, 2, 5
+    q, k, v = _rand(rng, B, S, H_q, d), _rand(rng, B, S, H_kv, d), _rand(rng, B, S, H_kv, d)
+    dout = _rand(rng, B, S, H_q, d)
+    for causal in (False, True):
+        dq, dk, dv = oracle.attention_grad(q, k, v, dout, 0.5, causal=causal)
+        np.testing.assert_allclose(dk.sum(axis=1), 0.0, atol=1e-12)
+        group_dout = dout.reshape(B, S, H_kv, H_q // H_kv, d).sum(axis=3).sum(axis=1)
+        np.testing.assert_allclose(dv.sum(axis=1), group_dout, rtol=1e-12, atol=1e-12)
+
+
+def test_grad_zero_queries_closed_form():
+    """q = 0: uniform weights; dq_i = scale * sum_j p_j (dp_j - D_i) k_j with p = 1/n."""
+    rng = np.random.default_rng(43)
+    B, S, H, d = 1, 6, 1, 3
+    q = np.zeros((B, S, H, d))
+    k, v, dout = _rand(rng, B, S, H, d), _rand(rng, B, S, H, d), _rand(rng, B, S, H, d)
+    dq, dk, dv = oracle.attention_grad(q, k, v, dout, 0.9)
+    dp = dout[0, :, 0] @ v[0, :, 0].T                     # [i, j]
+    D = dp.mean(axis=1, keepdims=True)
+    expect = 0.9 * ((dp - D) / S) @ k[0, :, 0]
+    np.testing.assert_allclose(dq[0, :, 0], expect, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dk, 0.0, atol=1e-15)       # ds_ij * q_i with q = 0
+    # p = 1/S for every pair, so every dv_j is the mean of the upstream rows
+    np.testing.assert_allclose(dv[0, :, 0], np.tile(dout[0, :, 0].mean(axis=0), (S, 1)), rtol=1e-12)
