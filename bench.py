@@ -25,7 +25,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_FP32_TFLOPS = 157.3
-KERNEL_SOURCES = ["reduced_query_head_amd/csrc/attn_fwd.hip", "reduced_query_head_amd/csrc/api.cpp"]
+KERNEL_SOURCES = ["reduced_query_head_amd/csrc/attn_fwd.hip", "reduced_query_head_amd/csrc/device_common.h"]
 
 
 def algorithmic_flops(B, S, H_q, d, causal):

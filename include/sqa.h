@@ -107,6 +107,43 @@ sqa_status sqa_attn_fwd_lse(const void* q, const void* k, const void* v, void* o
                             int64_t B, int64_t S, int32_t H_q, int32_t H_kv, int32_t d,
                             sqa_dtype dtype, float scale, int causal, sqa_stream_t stream);
 
+/*
+ * Attention backward: gradients of out with respect to q, k and v for the
+ * upstream gradient dout = dL/dout.  The pages define only the forward
+ * computation; this is its exact derivative (softmax Jacobian), with the
+ * gradients of a shared K/V head summed over the H_q/H_kv query heads that
+ * read it (GQA explainer: grouping figure, expand in the PyTorch module):
+ *
+ *   P = exp(scale*q.k - lse), dP = dout.v, D_i = <dout_i, out_i>,
+ *   dS = P (dP - D), dq = scale dS k, dk = scale dS^T q, dv = P^T dout.
+ *
+ *   q, k, v, out, dout   the forward's inputs and output and the upstream
+ *                        gradient (dout shaped like out), dtype elements,
+ *                        16-byte aligned, BSHD as in sqa_attn_fwd
+ *   lse                  [B, S, H_q] fp32 from sqa_attn_fwd_lse, 4-byte aligned
+ *   dq                   [B, S, H_q, d] output, written in full
+ *   dk, dv               [B, S, H_kv, d] outputs, written in full
+ *   workspace            caller-owned scratch of at least
+ *                        sqa_attn_bwd_workspace_size(B, S, H_q) bytes,
+ *                        16-byte aligned; contents are overwritten
+ *   workspace_bytes      its size
+ *   B ... stream         as for sqa_attn_fwd (same scale and causal as the
+ *                        forward that produced out and lse)
+ *
+ * Outputs and workspace must not overlap each other or any input.  Errors as
+ * for sqa_attn_fwd; SQA_ERR_UNSUPPORTED also when the workspace would reach
+ * 4 GiB.  bf16: MFMA kernels with fp32 accumulation, probabilities and dS
+ * rounded to bf16 for the products; fp32: plain fp32 arithmetic.
+ */
+sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                        int64_t workspace_bytes, int64_t B, int64_t S, int32_t H_q, int32_t H_kv,
+                        int32_t d, sqa_dtype dtype, float scale, int causal, sqa_stream_t stream);
+
+/* Workspace bytes sqa_attn_bwd needs (2 fp32 values per query row and head,
+ * rows padded to a multiple of 64); -1 for invalid sizes. */
+int64_t sqa_attn_bwd_workspace_size(int64_t B, int64_t S, int32_t H_q);
+
 /* Static, NUL-terminated description of a status code. */
 const char* sqa_status_string(sqa_status status);
 

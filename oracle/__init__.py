@@ -41,6 +41,9 @@ def _load():
         lib.sqa_oracle_bwd.restype = ctypes.c_int
         lib.sqa_oracle_bwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, i64, i64, i32, i32, i32,
                                        ctypes.c_double, ctypes.c_int, ctypes.c_int]
+        lib.sqa_oracle_bwd_dq_rows.restype = ctypes.c_int
+        lib.sqa_oracle_bwd_dq_rows.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, i64, i64, i32, i32, i32,
+                                               ctypes.c_double, ctypes.c_int, vp, i64, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -134,3 +137,23 @@ def attention_grad(q, k, v, dout, scale, causal=False, n_threads=0):
     if rc != 0:
         raise MemoryError("oracle: allocation failed")
     return dq, dk, dv
+
+
+def attention_grad_dq_rows(q, k, v, dout, scale, rows, causal=False, n_threads=0):
+    """fp64 dq at the query positions `rows` only: [B, len(rows), H_q, d]."""
+    arrs = [np.ascontiguousarray(a) for a in (q, k, v, dout)]
+    q, k, v, dout = arrs
+    if len({a.dtype for a in arrs}) != 1 or q.dtype not in _DTYPE_CODE:
+        raise TypeError("q, k, v, dout must share one dtype")
+    B, S, H_q, d = q.shape
+    H_kv = k.shape[2]
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.zeros((B, rows.size, H_q, d), dtype=np.float64)
+    ptr = lambda a: ctypes.c_void_p(a.ctypes.data)
+    rc = _load().sqa_oracle_bwd_dq_rows(ptr(q), ptr(k), ptr(v), ptr(dout), _DTYPE_CODE[q.dtype], ptr(out), B, S, H_q,
+                                        H_kv, d, float(scale), 1 if causal else 0, ptr(rows), rows.size, int(n_threads))
+    if rc == -1:
+        raise ValueError("oracle: invalid arguments")
+    if rc != 0:
+        raise MemoryError("oracle: allocation failed")
+    return out

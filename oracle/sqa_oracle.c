@@ -336,3 +336,74 @@ int sqa_oracle_bwd(const void* q, const void* k, const void* v, const void* dout
   free(Dd);
   return 0;
 }
+
+/*
+ * dq rows only (pass 1 of sqa_oracle_bwd restricted to the query positions
+ * `rows`, all batches and heads): dq_out is fp64 [B, n_rows, H_q, d].  Each
+ * row needs only its own keys, so a sample of rows costs a sample of the work.
+ */
+int sqa_oracle_bwd_dq_rows(const void* q, const void* k, const void* v, const void* dout, int dtype, double* dq_out,
+                           int64_t B, int64_t S, int32_t H_q, int32_t H_kv, int32_t d, double scale, int causal,
+                           const int64_t* rows, int64_t n_rows, int n_threads) {
+  if (B < 0 || S < 0 || H_q < 1 || H_kv < 1 || d < 1 || H_q % H_kv != 0) return -1;
+  if (dtype < 0 || dtype > 2 || (causal != 0 && causal != 1) || !rows || n_rows < 0) return -1;
+  for (int64_t r = 0; r < n_rows; ++r)
+    if (rows[r] < 0 || rows[r] >= S) return -1;
+  const int64_t items = B * n_rows * (int64_t)H_q;
+  if (items == 0) return 0;
+  const int32_t R = H_q / H_kv;
+  int failed = 0;
+#ifdef _OPENMP
+  if (n_threads <= 0) n_threads = omp_get_max_threads();
+#else
+  n_threads = 1;
+#endif
+#pragma omp parallel num_threads(n_threads)
+  {
+    double* s = (double*)malloc((size_t)S * sizeof(double));
+    double* dp = (double*)malloc((size_t)S * sizeof(double));
+    if (!s || !dp) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < items; ++t) {
+      if (!s || !dp) continue;
+      const int64_t b = t / (n_rows * H_q);
+      const int64_t r = (t / H_q) % n_rows;
+      const int32_t h = (int32_t)(t % H_q);
+      const int64_t i = rows[r];
+      const int32_t g = h / R;
+      const int64_t last = causal ? i : S - 1;
+      const int64_t qo = ((b * S + i) * H_q + h) * (int64_t)d;
+      double m = -INFINITY;
+      for (int64_t j = 0; j <= last; ++j) {
+        const int64_t ko = ((b * S + j) * H_kv + g) * (int64_t)d;
+        double dot = 0.0, dd = 0.0;
+        for (int32_t e = 0; e < d; ++e) {
+          dot += load_elem(q, dtype, qo + e) * load_elem(k, dtype, ko + e);
+          dd += load_elem(dout, dtype, qo + e) * load_elem(v, dtype, ko + e);
+        }
+        s[j] = scale * dot;
+        dp[j] = dd;
+        if (s[j] > m) m = s[j];
+      }
+      double l = 0.0;
+      for (int64_t j = 0; j <= last; ++j) l += exp(s[j] - m);
+      const double L = m + log(l);
+      double Di = 0.0;
+      for (int64_t j = 0; j <= last; ++j) Di += exp(s[j] - L) * dp[j];
+      double* o = dq_out + ((b * n_rows + r) * H_q + h) * (int64_t)d;
+      for (int32_t e = 0; e < d; ++e) o[e] = 0.0;
+      for (int64_t j = 0; j <= last; ++j) {
+        const double ds = exp(s[j] - L) * (dp[j] - Di);
+        const int64_t ko = ((b * S + j) * H_kv + g) * (int64_t)d;
+        for (int32_t e = 0; e < d; ++e) o[e] += ds * load_elem(k, dtype, ko + e);
+      }
+      for (int32_t e = 0; e < d; ++e) o[e] *= scale;
+    }
+    free(s);
+    free(dp);
+  }
+  return failed ? -2 : 0;
+}

@@ -39,6 +39,11 @@ def load_library(path=None):
     lib.sqa_attn_fwd_lse.restype = ctypes.c_int
     lib.sqa_attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ctypes.c_int, ctypes.c_float,
                                      ctypes.c_int, vp]
+    lib.sqa_attn_bwd.restype = ctypes.c_int
+    lib.sqa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, ctypes.c_int,
+                                 ctypes.c_float, ctypes.c_int, vp]
+    lib.sqa_attn_bwd_workspace_size.restype = i64
+    lib.sqa_attn_bwd_workspace_size.argtypes = [i64, i64, i32]
     lib.sqa_status_string.restype = ctypes.c_char_p
     lib.sqa_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -111,3 +116,58 @@ def attn_fwd(q, k, v, out=None, scale=None, causal=False, stream=None, return_ls
     if st != SQA_OK:
         raise SqaError(st, status_string(st))
     return out
+
+
+def attn_bwd_workspace_size(B, S, H_q):
+    return int(load_library().sqa_attn_bwd_workspace_size(B, S, H_q))
+
+
+def attn_bwd_raw(q, k, v, out, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, S, H_q, H_kv, d, dtype, scale,
+                 causal, stream):
+    """Direct call of sqa_attn_bwd with integer device addresses; returns the status."""
+    return load_library().sqa_attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, S, H_q,
+                                       H_kv, d, dtype, scale, int(causal), stream)
+
+
+def attn_bwd(q, k, v, out, dout, lse, scale=None, causal=False, stream=None, dq=None, dk=None, dv=None,
+             workspace=None):
+    """Gradients (dq, dk, dv) of attn_fwd's output for upstream gradient dout.
+
+    q, k, v, out and lse as given to / returned by attn_fwd(..., return_lse=True)
+    with the same scale and causal flag; dout shaped like out.  Returns new
+    tensors unless dq, dk, dv are given.  A uint8 workspace of
+    attn_bwd_workspace_size(B, S, H_q) bytes is allocated if none is given.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-d GPU tensor")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype):
+        raise ValueError("q, k, v, out, dout must share one dtype")
+    dtype = SQA_BF16 if q.dtype == torch.bfloat16 else SQA_FP32 if q.dtype == torch.float32 else None
+    if dtype is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    B, S, H_q, d = q.shape
+    H_kv = k.shape[2]
+    if out.shape != q.shape or dout.shape != q.shape or k.shape != v.shape or tuple(k.shape[:2]) != (B, S):
+        raise ValueError("shape mismatch")
+    if lse.shape != (B, S, H_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of shape [B, S, H_q]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    ws_bytes = attn_bwd_workspace_size(B, S, H_q)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = attn_bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(), B, S, H_q,
+                      H_kv, d, dtype, float(scale), causal, handle)
+    if st != SQA_OK:
+        raise SqaError(st, status_string(st))
+    return dq, dk, dv

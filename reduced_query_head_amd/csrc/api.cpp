@@ -104,3 +104,77 @@ SQA_API sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, voi
                                 float scale, int causal, sqa_stream_t stream) {
   return sqa_attn_fwd_lse(q, k, v, out, nullptr, B, S, H_q, H_kv, d, dtype, scale, causal, stream);
 }
+
+SQA_API int64_t sqa_attn_bwd_workspace_size(int64_t B, int64_t S, int32_t H_q) {
+  if (B < 0 || S < 0 || H_q < 1) return -1;
+  return sqa::bwd_workspace_bytes(B, S, H_q);
+}
+
+SQA_API sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                                int64_t workspace_bytes, int64_t B, int64_t S, int32_t H_q, int32_t H_kv,
+                                int32_t d, sqa_dtype dtype, float scale, int causal, sqa_stream_t stream) {
+  if (B < 0 || S < 0 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0) return SQA_ERR_INVALID_ARGUMENT;
+  if (dtype != SQA_BF16 && dtype != SQA_FP32) return SQA_ERR_INVALID_ARGUMENT;
+  if (causal != 0 && causal != 1) return SQA_ERR_INVALID_ARGUMENT;
+  if (!isfinite(scale) || d < 1) return SQA_ERR_INVALID_ARGUMENT;
+  if (B == 0 || S == 0) return SQA_OK;
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !workspace) return SQA_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)dout | (uintptr_t)dq |
+       (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)workspace) & 15u)
+    return SQA_ERR_INVALID_ARGUMENT;
+  if ((uintptr_t)lse & 3u) return SQA_ERR_INVALID_ARGUMENT;
+  const int64_t elem = dtype == SQA_BF16 ? 2 : 4;
+  int64_t rows, q_elems, kv_elems, q_bytes, kv_bytes, lse_bytes;
+  if (!mul_ok(B, S, &rows) || !mul_ok(rows, (int64_t)H_q * d, &q_elems) ||
+      !mul_ok(rows, (int64_t)H_kv * d, &kv_elems) || !mul_ok(q_elems, elem, &q_bytes) ||
+      !mul_ok(kv_elems, elem, &kv_bytes) || !mul_ok(rows, (int64_t)H_q * 4, &lse_bytes))
+    return SQA_ERR_INVALID_ARGUMENT;
+  const int64_t ws_need = sqa::bwd_workspace_bytes(B, S, H_q);
+  if (workspace_bytes < ws_need) return SQA_ERR_INVALID_ARGUMENT;
+  // outputs and workspace must not overlap each other or any input
+  const void* ins[6] = {q, k, v, out, dout, lse};
+  const int64_t in_bytes[6] = {q_bytes, kv_bytes, kv_bytes, q_bytes, q_bytes, lse_bytes};
+  const void* outs[4] = {dq, dk, dv, workspace};
+  const int64_t out_bytes[4] = {q_bytes, kv_bytes, kv_bytes, ws_need};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (ranges_overlap(outs[i], out_bytes[i], ins[j], in_bytes[j])) return SQA_ERR_INVALID_ARGUMENT;
+    for (int j = i + 1; j < 4; ++j)
+      if (ranges_overlap(outs[i], out_bytes[i], outs[j], out_bytes[j])) return SQA_ERR_INVALID_ARGUMENT;
+  }
+  if (d != 32 && d != 64 && d != 128) return SQA_ERR_UNSUPPORTED;
+  if (S > (int64_t)1 << 30) return SQA_ERR_UNSUPPORTED;
+  // the statistics copies address the workspace with 32-bit byte offsets
+  if (ws_need >= ((int64_t)1 << 32)) return SQA_ERR_UNSUPPORTED;
+  if (dtype == SQA_BF16 ? sqa::bwd_grid_size(B, S, H_q, H_kv) > INT32_MAX
+                        : (rows * H_q + 255) / 256 > INT32_MAX)
+    return SQA_ERR_UNSUPPORTED;
+
+  sqa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.workspace = workspace;
+  a.B = B;
+  a.S = S;
+  a.H_q = H_q;
+  a.H_kv = H_kv;
+  a.d = d;
+  a.dtype = dtype == SQA_BF16 ? 0 : 1;
+  const float log2e = 1.4426950408889634f;
+  const float mag = fabsf(scale);
+  a.c = mag > 0.f ? mag * log2e : 1e-30f;
+  if (!isfinite(a.c)) return SQA_ERR_INVALID_ARGUMENT;
+  a.negate_q = scale < 0.f;
+  a.scale = scale;
+  a.causal = causal;
+  a.stream = (void*)stream;
+  return sqa::launch_attn_bwd(a) == hipSuccess ? SQA_OK : SQA_ERR_HIP;
+}

@@ -1,0 +1,618 @@
+// Decoupled-head attention backward for gfx950 (MI355X, CDNA4).
+//
+// Gradients of out = softmax(scale * Q K^T) V (per query head h, with K/V head
+// g = floor(h / R) shared by the R query heads of its group, as in the GQA
+// explainer's grouping figure and expand) for an upstream gradient dO:
+//
+//   P = exp(scale * S - lse),  dP = dO V^T,  D_i = <dO_i, O_i>,
+//   dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q,  dV = P^T dO,
+//
+// where lse is the row log-normaliser the forward returns and dK, dV sum over
+// the query heads of a group.  Three kernels:
+//
+//  * bwd_stats: D_i = <dO_i, O_i> and lse_i * log2(e), written per (b, head)
+//    as contiguous, 64-padded rows of a caller-provided workspace.
+//  * bwd_dq: one wave per 32 query rows of one head; K/V tiles of 64 keys
+//    staged in LDS for the whole K/V group (as in the forward).  With keys
+//    along MFMA M (S^T = K Q^T, dP^T = V dO^T) each lane owns one query, so
+//    D_i and lse_i are per-lane scalars; dQ^T += K^T dS^T reads K^T with
+//    transposing LDS reads.
+//  * bwd_dkdv: one wave per 32 keys of one K/V head, K and V held in
+//    registers; query tiles of 64 rows (Q, dO and their statistics) of all R
+//    query heads of the group stream through LDS.  S = Q K^T and dP = dO V^T
+//    put keys on lanes, so dV^T += dO^T P and dK^T += Q^T dS take P and dS
+//    straight from the accumulators and dO^T, Q^T from transposing LDS reads.
+//
+// All matrix products are bf16 MFMA with fp32 accumulation; P and dS are
+// rounded to bf16 for the products that consume them.  The fp32 path is plain
+// VALU arithmetic for exactness checks at small sizes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace sqa {
+namespace {
+
+using namespace dev;
+
+constexpr int kRows32 = 32;  // query rows (dq) or keys (dk/dv) per wave
+constexpr int kTile = 64;    // K/V tile (dq) and Q/dO tile (dk/dv) length
+constexpr int kWaves = 4;
+
+__host__ __device__ constexpr int64_t pad64(int64_t s) { return (s + 63) / 64 * 64; }
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;
+  float* ws_lse2;    // [B, H_q, S_pad]: lse * log2(e)
+  float* ws_delta;   // [B, H_q, S_pad]: <dO_i, O_i>
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int S;
+  int S_pad;
+  int H_q;
+  int H_kv;
+  int R;
+  int n_groups;      // B * H_kv
+  int n_items;       // dq: R * ceil(S / 32) per group
+  int chunks;        // dq: workgroups per group
+  int key_blocks;    // dk/dv: workgroups per group
+  float c;           // |scale| * log2(e)
+  float scale;       // signed scale
+  uint32_t q_sign;   // 0x8000 when scale < 0: q (dq kernel) or k (dk/dv kernel) negated on load, exact
+};
+
+// ---------------------------------------------------------------------------
+// stats: delta and lse2 rows, transposed to [B, H_q, S_pad]; pad entries 0.
+// 8 lanes per (b, i, h) row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_stats_bf16(BwdParams p, int64_t B) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid >> 3;  // over B * S_pad * H_q, ordered (b, h, i)
+  const int sub = (int)(gid & 7);
+  const int64_t total = B * p.H_q * (int64_t)p.S_pad;
+  float acc = 0.f;
+  int64_t b = 0, h = 0, i = 0;
+  if (row < total) {
+    i = row % p.S_pad;
+    h = (row / p.S_pad) % p.H_q;
+    b = row / ((int64_t)p.S_pad * p.H_q);
+    if (i < p.S) {
+      const int64_t off = ((b * p.S + i) * p.H_q + h) * D;
+      for (int cc = sub; cc < D / 8; cc += 8) {
+        const u32x4 ov = *(const u32x4*)(p.o + off + cc * 8);
+        const u32x4 gv = *(const u32x4*)(p.dout + off + cc * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc += __uint_as_float(ov[e] << 16) * __uint_as_float(gv[e] << 16);
+          acc += __uint_as_float(ov[e] & 0xFFFF0000u) * __uint_as_float(gv[e] & 0xFFFF0000u);
+        }
+      }
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  if (row < total && sub == 0) {
+    const bool valid = i < p.S;
+    p.ws_delta[row] = valid ? acc : 0.f;
+    p.ws_lse2[row] = valid ? p.lse[(b * p.S + i) * p.H_q + h] * 1.4426950408889634f : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: 4 waves per workgroup, one 32-row item each (as in the forward).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdParams p) {
+  constexpr int WAVES = kWaves, KEYS = kTile;
+  constexpr int KS = D / 16, DB = D / 32, NB = KEYS / 32, NT = KEYS / 16;
+  constexpr int TILE = KEYS * D;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v1[TILE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int S = p.S;
+
+  const int grp = blockIdx.x % p.n_groups;
+  const int ord = blockIdx.x / p.n_groups;
+  const int chunk = CAUSAL ? (p.chunks - 1 - ord) : ord;
+  const int b = grp / p.H_kv;
+  const int g = grp % p.H_kv;
+  const int item = chunk * WAVES + wave;
+  const bool active = item < p.n_items;
+  const int pos0 = (item / p.R) * kRows32;
+  const int h = active ? g * p.R + item % p.R : 0;
+  const int last_item = min(chunk * WAVES + WAVES - 1, p.n_items - 1);
+  const int wg_last_pos = min((last_item / p.R) * kRows32 + kRows32 - 1, S - 1);
+  const int n_tiles = CAUSAL ? wg_last_pos / KEYS + 1 : (S + KEYS - 1) / KEYS;
+
+  const int64_t kv_stride = (int64_t)p.H_kv * D;
+  const uint16_t* k_base = p.k + ((int64_t)b * S * p.H_kv + g) * D;
+  const uint16_t* v_base = p.v + ((int64_t)b * S * p.H_kv + g) * D;
+  TileCopy<D, WAVES, KEYS> cp;
+  cp.init(kv_stride, wave, lane);
+  cp.issue(k_base, kv_stride, S, (SQA_LDS uint16_t*)lds_k0, wave);
+  cp.issue(v_base, kv_stride, S, (SQA_LDS uint16_t*)lds_v0, wave);
+
+  // Q^T and dO^T as B operands: lane holds query pos0 + col, dims ks*16 + half*8 ...
+  const int qrow = min(pos0 + col, S - 1);
+  bf16x8 qf[KS], gf[KS];
+  {
+    const int64_t off = (((int64_t)b * S + qrow) * p.H_q + h) * D + half * 8;
+    const uint32_t sgn = p.q_sign * 0x10001u;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 raw = *(const u32x4*)(p.q + off + ks * 16);
+      raw ^= (u32x4){sgn, sgn, sgn, sgn};
+      qf[ks] = __builtin_bit_cast(bf16x8, raw);
+      gf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(p.dout + off + ks * 16));
+    }
+  }
+  const int64_t srow = ((int64_t)b * p.H_q + h) * p.S_pad + qrow;
+  const float lse2 = p.ws_lse2[srow];
+  const float delta = p.ws_delta[srow];
+
+  int k_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = tile_off<D>(col, ks * 16 + half * 8);
+  int t_off[DB][2];
+  {
+    const int grp16 = lane >> 4, i16 = lane & 15, e = i16 >> 2, c4 = i16 & 3;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) t_off[db][j] = tile_off<D>(4 * half + 8 * j + e, db * 32 + (grp16 & 1) * 16 + 4 * c4);
+  }
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = (f32x16){};
+  const float c = p.c;
+  const int my_q = pos0 + col;
+  const int wave_last = pos0 + kRows32 - 1;
+
+  auto step = [&](int t, SQA_LDS uint16_t* kt, SQA_LDS uint16_t* vt, SQA_LDS uint16_t* kn, SQA_LDS uint16_t* vn) {
+    const int kv0 = t * KEYS;
+    wait_copies();
+    __syncthreads();
+    if (t + 1 < n_tiles) {
+      const int64_t nxt = (int64_t)(kv0 + KEYS) * kv_stride;
+      cp.issue(k_base + nxt, kv_stride, S - kv0 - KEYS, kn, wave);
+      cp.issue(v_base + nxt, kv_stride, S - kv0 - KEYS, vn, wave);
+    }
+    if (!active || (CAUSAL && kv0 > wave_last)) return;
+    // S^T = K Q^T and dP^T = V dO^T (keys along M, this lane's query along N)
+    f32x16 s[NB], dp[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) s[nb] = dp[nb] = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const bf16x8 a = *(const SQA_LDS bf16x8*)(kt + nb * 32 * D + k_off[ks]);
+        s[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[nb], 0, 0, 0);
+        const bf16x8 bv = *(const SQA_LDS bf16x8*)(vt + nb * 32 * D + k_off[ks]);
+        dp[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, gf[ks], dp[nb], 0, 0, 0);
+      }
+    lds_mfma_pipeline_hint<2 * KS * NB, 1, 4>();
+    // P = 2^(c s - lse2), masked keys 0; dS = P (dP - D); key of s[nb][r] is
+    // kv0 + 4*half + nb*32 + 8*(r/4) + r%4
+    const bool need_mask = (kv0 + KEYS > S) || (CAUSAL && kv0 + KEYS - 1 > pos0);
+    const int lim = (CAUSAL ? min(my_q, S - 1) : S - 1) - kv0 - 4 * half;
+    bf16x8 dsk[NT];
+#pragma unroll
+    for (int st = 0; st < NT; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int nb = st >> 1, r = (st & 1) * 8 + e;
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][r], c, -lse2));
+        if (need_mask && (nb * 32 + 8 * (r >> 2) + (r & 3) > lim)) pv = 0.f;
+        dsk[st][e] = (__bf16)(pv * (dp[nb][r] - delta));
+      }
+    // dQ^T += K^T dS^T (K^T from transposing reads of the K tile)
+#pragma unroll
+    for (int st = 0; st < NT; ++st)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SQA_LDS bf16x4*)(kt + st * 16 * D + t_off[db][0]));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SQA_LDS bf16x4*)(kt + st * 16 * D + t_off[db][1]));
+        const bf16x8 ka = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, dsk[st], acc[db], 0, 0, 0);
+      }
+    lds_mfma_pipeline_hint<NT * DB, 2, 4>();
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, (SQA_LDS uint16_t*)lds_k0, (SQA_LDS uint16_t*)lds_v0, (SQA_LDS uint16_t*)lds_k1, (SQA_LDS uint16_t*)lds_v1);
+    if (t + 1 < n_tiles)
+      step(t + 1, (SQA_LDS uint16_t*)lds_k1, (SQA_LDS uint16_t*)lds_v1, (SQA_LDS uint16_t*)lds_k0, (SQA_LDS uint16_t*)lds_v0);
+  }
+
+  if (!active || my_q >= S) return;
+  uint16_t* op = p.dq + (((int64_t)b * S + my_q) * p.H_q + h) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[db][4 * j + e] * p.scale);
+      *(bf16x4*)(op + db * 32 + 8 * j + 4 * half) = w;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: 4 waves per workgroup, 32 keys per wave (128 keys per workgroup).
+// Copies of one query tile: Q rows and dO rows of head h (TileCopy), plus
+// 256-byte runs of lse2 and delta: lanes 0-15 and 16-31 of one extra copy
+// (lanes 32-63 repeat the lse2 run into the unused upper half).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
+  constexpr int WAVES = kWaves, QT = kTile;
+  constexpr int KS = D / 16, DB = D / 32;
+  constexpr int TILE = QT * D;
+  constexpr int KEYS_WG = WAVES * kRows32;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_q0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_q1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_g0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_g1[TILE];
+  __shared__ __attribute__((aligned(1024))) float lds_s0[256];  // [0,64) lse2, [64,128) delta
+  __shared__ __attribute__((aligned(1024))) float lds_s1[256];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int S = p.S;
+
+  const int grp = blockIdx.x % p.n_groups;
+  const int kb = blockIdx.x / p.n_groups;  // low keys first: they see the most queries when causal
+  const int b = grp / p.H_kv;
+  const int g = grp % p.H_kv;
+  const int key_wg0 = kb * KEYS_WG;
+  const int key0 = key_wg0 + wave * kRows32;
+  const int my_key = key0 + col;
+
+  // query tiles: R heads x tiles from the first one that can see this block
+  const int qt_first = CAUSAL ? key_wg0 / QT : 0;
+  const int qt_count = (S + QT - 1) / QT - qt_first;
+  const int U = p.R * qt_count;
+
+  const int64_t q_stride = (int64_t)p.H_q * D;
+  TileCopy<D, WAVES, QT> cp;
+  cp.init(q_stride, wave, lane);
+  // per-lane stats copy offset (bytes from ws base) for the tile of (h, qt)
+  const float* ws = p.ws_lse2;
+  const uint32_t delta_shift = (uint32_t)((p.ws_delta - p.ws_lse2) * 4);
+  const uint32_t stat_lane = lane < 16 ? lane * 16u : lane < 32 ? delta_shift + (lane - 16) * 16u : (lane & 15) * 16u;
+
+  auto issue_tile = [&](int u, SQA_LDS uint16_t* qd, SQA_LDS uint16_t* gd, SQA_LDS float* sd) {
+    const int hl = u / qt_count;
+    const int qt = qt_first + u % qt_count;
+    const int h = g * p.R + hl;
+    const int64_t base = (((int64_t)b * S + qt * QT) * p.H_q + h) * D;
+    cp.issue(p.q + base, q_stride, S - qt * QT, qd, wave);
+    cp.issue(p.dout + base, q_stride, S - qt * QT, gd, wave);
+    if (wave == 0) {
+      const int64_t srow = ((int64_t)b * p.H_q + h) * p.S_pad + qt * QT;
+      dma16(ws, (uint32_t)(srow * 4) + stat_lane, lds_addr(sd));
+    }
+  };
+
+  // K^T and V^T as B operands: lane holds key my_key, dims ks*16 + half*8 ...
+  // A negative scale is folded into k here (q streams through LDS unchanged),
+  // so that c * s = scale * log2(e) * <q, k> with c = |scale| * log2(e).
+  bf16x8 kf[KS], vf[KS];
+  {
+    const int krow = min(my_key, S - 1);
+    const int64_t off = (((int64_t)b * S + krow) * p.H_kv + g) * D + half * 8;
+    const uint32_t sgn = p.q_sign * 0x10001u;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 raw = *(const u32x4*)(p.k + off + ks * 16);
+      raw ^= (u32x4){sgn, sgn, sgn, sgn};
+      kf[ks] = __builtin_bit_cast(bf16x8, raw);
+      vf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(p.v + off + ks * 16));
+    }
+  }
+  if (U > 0) issue_tile(0, (SQA_LDS uint16_t*)lds_q0, (SQA_LDS uint16_t*)lds_g0, (SQA_LDS float*)lds_s0);
+
+  int a_off[KS];  // Q / dO rows as the A operand: row col of the 32-row half
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) a_off[ks] = tile_off<D>(col, ks * 16 + half * 8);
+  int t_off[DB][2];  // transposing reads of the Q / dO tile
+  {
+    const int grp16 = lane >> 4, i16 = lane & 15, e = i16 >> 2, c4 = i16 & 3;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) t_off[db][j] = tile_off<D>(4 * half + 8 * j + e, db * 32 + (grp16 & 1) * 16 + 4 * c4);
+  }
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dk[db] = dv[db] = (f32x16){};
+  const float c = p.c;
+
+  auto step = [&](int u, SQA_LDS uint16_t* qt_l, SQA_LDS uint16_t* gt_l, SQA_LDS float* st_l, SQA_LDS uint16_t* qn,
+                  SQA_LDS uint16_t* gn, SQA_LDS float* sn) {
+    wait_copies();
+    __syncthreads();
+    if (u + 1 < U) issue_tile(u + 1, qn, gn, sn);
+    const int qt = qt_first + u % qt_count;
+    const int q0 = qt * QT;
+    if (CAUSAL && q0 + QT - 1 < key0) return;  // whole tile before this wave's keys
+#pragma unroll
+    for (int qh = 0; qh < QT / 32; ++qh) {
+      const int qbase = q0 + qh * 32;
+      if (CAUSAL && qbase + 31 < key0) continue;
+      // S = Q K^T and dP = dO V^T (queries along M, this lane's key along N)
+      f32x16 s = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = *(const SQA_LDS bf16x8*)(qt_l + qh * 32 * D + a_off[ks]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], s, 0, 0, 0);
+        const bf16x8 ga = *(const SQA_LDS bf16x8*)(gt_l + qh * 32 * D + a_off[ks]);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
+      }
+      lds_mfma_pipeline_hint<2 * KS, 1, 4>();
+      // query of register r: qbase + 8*(r/4) + 4*half + r%4
+      float l2[16], dl[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 a = *(const SQA_LDS f32x4*)(st_l + qh * 32 + 8 * j + 4 * half);
+        const f32x4 d4 = *(const SQA_LDS f32x4*)(st_l + 64 + qh * 32 + 8 * j + 4 * half);
+        l2[4 * j] = a[0]; l2[4 * j + 1] = a[1]; l2[4 * j + 2] = a[2]; l2[4 * j + 3] = a[3];
+        dl[4 * j] = d4[0]; dl[4 * j + 1] = d4[1]; dl[4 * j + 2] = d4[2]; dl[4 * j + 3] = d4[3];
+      }
+      const bool need_mask = (qbase + 32 > S) || (CAUSAL && qbase < key0 + 31);
+      const int qlo = qbase + 4 * half;
+      bf16x8 pk[2], dsk[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = st * 8 + e;
+          const int qi = qlo + 8 * (r >> 2) + (r & 3);
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2[r]));
+          if (need_mask && ((qi >= S) || (CAUSAL && my_key > qi))) pv = 0.f;
+          pk[st][e] = (__bf16)pv;
+          dsk[st][e] = (__bf16)(pv * (dp[r] - dl[r]));
+        }
+      // dV^T += dO^T P and dK^T += Q^T dS (16 queries per MFMA step)
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int ro = (qh * 32 + st * 16) * D;
+          const bf16x4 glo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SQA_LDS bf16x4*)(gt_l + ro + t_off[db][0]));
+          const bf16x4 ghi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SQA_LDS bf16x4*)(gt_l + ro + t_off[db][1]));
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                           pk[st], dv[db], 0, 0, 0);
+          const bf16x4 qlo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SQA_LDS bf16x4*)(qt_l + ro + t_off[db][0]));
+          const bf16x4 qhi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SQA_LDS bf16x4*)(qt_l + ro + t_off[db][1]));
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(qlo4, qhi4, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                           dsk[st], dk[db], 0, 0, 0);
+        }
+      lds_mfma_pipeline_hint<4 * DB, 2, 4>();
+    }
+  };
+  for (int u = 0; u < U; u += 2) {
+    step(u, (SQA_LDS uint16_t*)lds_q0, (SQA_LDS uint16_t*)lds_g0, (SQA_LDS float*)lds_s0, (SQA_LDS uint16_t*)lds_q1,
+         (SQA_LDS uint16_t*)lds_g1, (SQA_LDS float*)lds_s1);
+    if (u + 1 < U)
+      step(u + 1, (SQA_LDS uint16_t*)lds_q1, (SQA_LDS uint16_t*)lds_g1, (SQA_LDS float*)lds_s1,
+           (SQA_LDS uint16_t*)lds_q0, (SQA_LDS uint16_t*)lds_g0, (SQA_LDS float*)lds_s0);
+  }
+
+  if (my_key >= S) return;
+  const int64_t off = (((int64_t)b * S + my_key) * p.H_kv + g) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x4 wk, wv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        wk[e] = (__bf16)(dk[db][4 * j + e] * p.scale);
+        wv[e] = (__bf16)dv[db][4 * j + e];
+      }
+      *(bf16x4*)(p.dk + off + db * 32 + 8 * j + 4 * half) = wk;
+      *(bf16x4*)(p.dv + off + db * 32 + 8 * j + 4 * half) = wv;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path: plain VALU loops in fp32 (small sizes; exactness checks).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_stats_f32(const float* o, const float* dout, const float* lse, float* ws_lse2,
+                                                     float* ws_delta, int64_t B, int S, int S_pad, int H_q) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (b, h, i) over S_pad
+  if (row >= B * H_q * (int64_t)S_pad) return;
+  const int64_t i = row % S_pad, h = (row / S_pad) % H_q, b = row / ((int64_t)S_pad * H_q);
+  if (i >= S) {
+    ws_lse2[row] = 0.f;
+    ws_delta[row] = 0.f;
+    return;
+  }
+  const int64_t off = ((b * S + i) * H_q + h) * D;
+  float acc = 0.f;
+  for (int e = 0; e < D; ++e) acc = __builtin_fmaf(o[off + e], dout[off + e], acc);
+  ws_delta[row] = acc;
+  ws_lse2[row] = lse[(b * S + i) * H_q + h] * 1.4426950408889634f;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dq_f32(const float* q, const float* k, const float* v, const float* dout,
+                                                  const float* ws_lse2, const float* ws_delta, float* dq, int64_t B,
+                                                  int S, int S_pad, int H_q, int H_kv, int R, float c, float scale,
+                                                  int causal) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (b, i, h)
+  if (t >= B * S * H_q) return;
+  const int h = (int)(t % H_q);
+  const int i = (int)((t / H_q) % S);
+  const int64_t b = t / ((int64_t)H_q * S);
+  const int g = h / R;
+  const int64_t srow = (b * H_q + h) * S_pad + i;
+  const float lse2 = ws_lse2[srow], delta = ws_delta[srow];
+  float acc[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) acc[e] = 0.f;
+  const float* qp = q + t * D;
+  const float* gp = dout + t * D;
+  const int last = causal ? i : S - 1;
+  for (int j = 0; j <= last; ++j) {
+    const float* kp = k + ((b * S + j) * H_kv + g) * D;
+    const float* vp = v + ((b * S + j) * H_kv + g) * D;
+    float s = 0.f, dp = 0.f;
+    for (int e = 0; e < D; ++e) {
+      s = __builtin_fmaf(qp[e], kp[e], s);
+      dp = __builtin_fmaf(gp[e], vp[e], dp);
+    }
+    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s, c, -lse2));
+    const float ds = pv * (dp - delta);
+#pragma unroll
+    for (int e = 0; e < D; ++e) acc[e] = __builtin_fmaf(ds, kp[e], acc[e]);
+  }
+  float* op = dq + t * D;
+#pragma unroll
+  for (int e = 0; e < D; ++e) op[e] = acc[e] * scale;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_f32(const float* q, const float* k, const float* v, const float* dout,
+                                                    const float* ws_lse2, const float* ws_delta, float* dk, float* dv,
+                                                    int64_t B, int S, int S_pad, int H_q, int H_kv, int R, float c,
+                                                    float scale, int causal) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (b, j, g)
+  if (t >= B * S * H_kv) return;
+  const int g = (int)(t % H_kv);
+  const int j = (int)((t / H_kv) % S);
+  const int64_t b = t / ((int64_t)H_kv * S);
+  const float* kp = k + t * D;
+  const float* vp = v + t * D;
+  float ak[D], av[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) ak[e] = av[e] = 0.f;
+  for (int h = g * R; h < (g + 1) * R; ++h)
+    for (int i = causal ? j : 0; i < S; ++i) {
+      const float* qp = q + ((b * S + i) * H_q + h) * D;
+      const float* gp = dout + ((b * S + i) * H_q + h) * D;
+      const int64_t srow = (b * H_q + h) * S_pad + i;
+      float s = 0.f, dp = 0.f;
+      for (int e = 0; e < D; ++e) {
+        s = __builtin_fmaf(qp[e], kp[e], s);
+        dp = __builtin_fmaf(gp[e], vp[e], dp);
+      }
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s, c, -ws_lse2[srow]));
+      const float ds = pv * (dp - ws_delta[srow]);
+#pragma unroll
+      for (int e = 0; e < D; ++e) {
+        av[e] = __builtin_fmaf(pv, gp[e], av[e]);
+        ak[e] = __builtin_fmaf(ds, qp[e], ak[e]);
+      }
+    }
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    dk[t * D + e] = ak[e] * scale;
+    dv[t * D + e] = av[e];
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_bf16_t(const BwdArgs& a) {
+  BwdParams p;
+  p.q = (const uint16_t*)a.q;
+  p.k = (const uint16_t*)a.k;
+  p.v = (const uint16_t*)a.v;
+  p.o = (const uint16_t*)a.out;
+  p.dout = (const uint16_t*)a.dout;
+  p.lse = a.lse;
+  p.S = (int)a.S;
+  p.S_pad = (int)pad64(a.S);
+  p.H_q = a.H_q;
+  p.H_kv = a.H_kv;
+  p.R = a.H_q / a.H_kv;
+  p.ws_lse2 = (float*)a.workspace;
+  p.ws_delta = (float*)a.workspace + a.B * a.H_q * (int64_t)p.S_pad;
+  p.dq = (uint16_t*)a.dq;
+  p.dk = (uint16_t*)a.dk;
+  p.dv = (uint16_t*)a.dv;
+  p.n_groups = (int)(a.B * a.H_kv);
+  p.n_items = p.R * (int)((a.S + kRows32 - 1) / kRows32);
+  p.chunks = (p.n_items + kWaves - 1) / kWaves;
+  p.key_blocks = (int)((a.S + kWaves * kRows32 - 1) / (kWaves * kRows32));
+  p.c = a.c;
+  p.scale = a.scale;
+  p.q_sign = a.negate_q ? 0x8000u : 0u;
+  hipStream_t st = (hipStream_t)a.stream;
+  const int64_t stat_threads = a.B * a.H_q * (int64_t)p.S_pad * 8;
+  hipLaunchKernelGGL((bwd_stats_bf16<D>), dim3((unsigned)((stat_threads + 255) / 256)), dim3(256), 0, st, p, a.B);
+  hipLaunchKernelGGL((bwd_dq_bf16<D, CAUSAL>), dim3((unsigned)((int64_t)p.n_groups * p.chunks)), dim3(kWaves * 64), 0,
+                     st, p);
+  hipLaunchKernelGGL((bwd_dkdv_bf16<D, CAUSAL>), dim3((unsigned)((int64_t)p.n_groups * p.key_blocks)),
+                     dim3(kWaves * 64), 0, st, p);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_f32_t(const BwdArgs& a) {
+  const int S_pad = (int)pad64(a.S);
+  float* ws_lse2 = (float*)a.workspace;
+  float* ws_delta = ws_lse2 + a.B * a.H_q * (int64_t)S_pad;
+  hipStream_t st = (hipStream_t)a.stream;
+  const float c = a.negate_q ? -a.c : a.c;
+  const int64_t nst = a.B * a.H_q * (int64_t)S_pad;
+  hipLaunchKernelGGL((bwd_stats_f32<D>), dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, st, (const float*)a.out,
+                     (const float*)a.dout, a.lse, ws_lse2, ws_delta, a.B, (int)a.S, S_pad, a.H_q);
+  const int64_t nq = a.B * a.S * a.H_q, nk = a.B * a.S * a.H_kv;
+  hipLaunchKernelGGL((bwd_dq_f32<D>), dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, st, (const float*)a.q,
+                     (const float*)a.k, (const float*)a.v, (const float*)a.dout, ws_lse2, ws_delta, (float*)a.dq, a.B,
+                     (int)a.S, S_pad, a.H_q, a.H_kv, a.H_q / a.H_kv, c, a.scale, a.causal);
+  hipLaunchKernelGGL((bwd_dkdv_f32<D>), dim3((unsigned)((nk + 255) / 256)), dim3(256), 0, st, (const float*)a.q,
+                     (const float*)a.k, (const float*)a.v, (const float*)a.dout, ws_lse2, ws_delta, (float*)a.dk,
+                     (float*)a.dv, a.B, (int)a.S, S_pad, a.H_q, a.H_kv, a.H_q / a.H_kv, c, a.scale, a.causal);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t bwd_workspace_bytes(int64_t B, int64_t S, int32_t H_q) { return 2 * B * (int64_t)H_q * pad64(S) * 4; }
+
+int64_t bwd_grid_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv) {
+  const int64_t items = (int64_t)(H_q / H_kv) * ((S + kRows32 - 1) / kRows32);
+  const int64_t a = B * H_kv * ((items + kWaves - 1) / kWaves);
+  const int64_t b = B * H_kv * ((S + kWaves * kRows32 - 1) / (kWaves * kRows32));
+  const int64_t c = (B * H_q * pad64(S) * 8 + 255) / 256;
+  return a > b ? (a > c ? a : c) : (b > c ? b : c);
+}
+
+hipError_t launch_attn_bwd(const BwdArgs& a) {
+  if (a.dtype == 0) {
+    switch (a.d) {
+      case 32: return a.causal ? launch_bwd_bf16_t<32, true>(a) : launch_bwd_bf16_t<32, false>(a);
+      case 64: return a.causal ? launch_bwd_bf16_t<64, true>(a) : launch_bwd_bf16_t<64, false>(a);
+      case 128: return a.causal ? launch_bwd_bf16_t<128, true>(a) : launch_bwd_bf16_t<128, false>(a);
+    }
+  } else {
+    switch (a.d) {
+      case 32: return launch_bwd_f32_t<32>(a);
+      case 64: return launch_bwd_f32_t<64>(a);
+      case 128: return launch_bwd_f32_t<128>(a);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sqa

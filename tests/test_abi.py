@@ -91,3 +91,34 @@ def test_lse_rejects_the_same_errors_as_forward():
     assert _call_lse(FAKE + (4 << 30), H_q=6, H_kv=4) == sqa.SQA_ERR_INVALID_ARGUMENT
     assert _call_lse(FAKE + (4 << 30), d=96) == sqa.SQA_ERR_UNSUPPORTED
     assert _call_lse(0, B=0, q=0, k=0, v=0, out=0) == sqa.SQA_OK
+
+
+def _call_bwd(**kw):
+    G = 1 << 32
+    a = dict(q=FAKE, k=FAKE + G, v=FAKE + 2 * G, out=FAKE + 3 * G, dout=FAKE + 4 * G, lse=FAKE + 5 * G,
+             dq=FAKE + 6 * G, dk=FAKE + 7 * G, dv=FAKE + 8 * G, ws=FAKE + 9 * G, ws_bytes=1 << 30, B=1, S=128,
+             H_q=8, H_kv=2, d=128, dtype=0, scale=0.088, causal=1)
+    a.update(kw)
+    return sqa.attn_bwd_raw(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"], a["ws"],
+                            a["ws_bytes"], a["B"], a["S"], a["H_q"], a["H_kv"], a["d"], a["dtype"], a["scale"],
+                            a["causal"], 0)
+
+
+def test_bwd_workspace_size():
+    assert sqa.attn_bwd_workspace_size(2, 100, 8) == 2 * 2 * 8 * 128 * 4
+    assert sqa.attn_bwd_workspace_size(1, 128, 1) == 2 * 128 * 4
+    assert sqa.attn_bwd_workspace_size(-1, 10, 1) == -1
+
+
+@pytest.mark.parametrize("kw", [
+    dict(H_q=6, H_kv=4), dict(dout=0), dict(lse=0), dict(ws=0), dict(dq=FAKE + 8), dict(lse=FAKE + (5 << 32) + 2),
+    dict(ws_bytes=2 * 8 * 128 * 4 - 1), dict(dq=FAKE + 64), dict(dk=FAKE + (6 << 32) + 128),
+    dict(ws=FAKE + (8 << 32) + 256), dict(causal=3), dict(scale=float("nan")),
+])
+def test_bwd_invalid(kw):
+    assert _call_bwd(**kw) == sqa.SQA_ERR_INVALID_ARGUMENT
+
+
+def test_bwd_unsupported_and_empty():
+    assert _call_bwd(d=80) == sqa.SQA_ERR_UNSUPPORTED
+    assert _call_bwd(B=0, q=0, k=0, v=0, out=0, dout=0, lse=0, dq=0, dk=0, dv=0, ws=0, ws_bytes=0) == sqa.SQA_OK

@@ -423,3 +423,15 @@ def test_grad_zero_queries_closed_form():
     np.testing.assert_allclose(dk, 0.0, atol=1e-15)       # ds_ij * q_i with q = 0
     # p = 1/S for every pair, so every dv_j is the mean of the upstream rows
     np.testing.assert_allclose(dv[0, :, 0], np.tile(dout[0, :, 0].mean(axis=0), (S, 1)), rtol=1e-12)
+
+
+def test_grad_dq_rows_equal_full_gradient_rows():
+    rng = np.random.default_rng(44)
+    B, S, H_q, H_kv, d = 2, 12, 4, 2, 5
+    q, k, v = _rand(rng, B, S, H_q, d), _rand(rng, B, S, H_kv, d), _rand(rng, B, S, H_kv, d)
+    dout = _rand(rng, B, S, H_q, d)
+    rows = np.array([11, 0, 5])
+    for causal in (False, True):
+        dq, _, _ = oracle.attention_grad(q, k, v, dout, 0.45, causal=causal)
+        sub = oracle.attention_grad_dq_rows(q, k, v, dout, 0.45, rows, causal=causal)
+        np.testing.assert_allclose(sub, dq[:, rows], rtol=1e-14, atol=1e-15)
