@@ -89,6 +89,47 @@ def time_variant(sqa, torch, w, variant, steps, warmup):
     return res
 
 
+def time_backward(sqa, torch, w, variant, steps, warmup):
+    """Times sqa.attn_bwd (row statistics, dq kernel, dk/dv kernel) on the
+    forward's own output and log-normaliser, with a seeded N(0,1) upstream
+    gradient.  Credited work: 10*d flops per visible (query, key) pair -- the
+    score recompute, dP = dO.V^T, dQ, dK and dV products -- 2.5x the forward."""
+    import inputs
+    import inputs.configs as cfg
+    v = w.variant(variant)
+    q, k, vv, _ = cfg.make_inputs(w, variant)
+    g = inputs.normal(w.seed(variant), 5, q.shape, "bf16", 1.0)
+    dq_, dk_, dv_, dg = (torch.from_numpy(a).view(torch.bfloat16).to("cuda") for a in (q, k, vv, g))
+    del q, k, vv, g
+    stream = torch.cuda.current_stream()
+    out, lse = sqa.attn_fwd(dq_, dk_, dv_, scale=w.scale, causal=w.causal, stream=stream, return_lse=True)
+    gq, gk, gv = torch.empty_like(dq_), torch.empty_like(dk_), torch.empty_like(dv_)
+    ws = torch.empty(sqa.attn_bwd_workspace_size(w.B, w.S, v.H_q), dtype=torch.uint8, device="cuda")
+
+    def run():
+        sqa.attn_bwd(dq_, dk_, dv_, out, dg, lse, scale=w.scale, causal=w.causal, stream=stream,
+                     dq=gq, dk=gk, dv=gv, workspace=ws)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        run()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    flops = algorithmic_flops(w.B, w.S, v.H_q, w.d, w.causal) * 10 // 4
+    ms = ev[0].elapsed_time(ev[steps]) / steps
+    del dq_, dk_, dv_, dg, out, lse, gq, gk, gv, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"{w.name}/{variant}", "flops_credited": flops, "ms_per_step": round(ms, 4),
+            "min_ms": round(min(per), 4), "max_ms": round(max(per), 4),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "pct_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "kernels": "bwd_stats_bf16 + bwd_dq_bf16 + bwd_dkdv_bf16 (one sqa_attn_bwd call)"}
+
+
 def gemm_context(torch, n=8192, iters=10):
     """A plain bf16 GEMM from the vendor library on random N(0,1) data, as a
     practical reference for dense bf16 throughput on this GPU (the chip is
@@ -152,6 +193,8 @@ def main():
     ap.add_argument("--comparators", default="auto",
                     help="comma list of variants timed beside it, 'auto' = all others, 'none'")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0 = skip)")
+    ap.add_argument("--backward", choices=["auto", "none", "only"], default="auto",
+                    help="time the backward too (auto: bf16 workloads), or only it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -181,6 +224,10 @@ def main():
 
     w = WORKLOADS[args.workload]
     sqa.load_library()
+    if args.backward == "only":
+        print(json.dumps({"backward": time_backward(sqa, torch, w, args.variant, args.steps, args.warmup)}),
+              flush=True)
+        return
     main_res = time_variant(sqa, torch, w, args.variant, args.steps, args.warmup)
     comps = {}
     names = [v.name for v in w.variants if v.name != args.variant] if args.comparators == "auto" else (
@@ -196,6 +243,8 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": traffic_from_profile(w.name, args.variant),
                 "kernel": f"attn_fwd_bf16<d={w.d},causal={int(w.causal)}>",
                 "flops_per_launch": main_res["flops"], "avg_launch_ms": round(main_res["avg_launch_ms"], 4)}
+    bwd = (time_backward(sqa, torch, w, args.variant, max(3, args.steps // 2), args.warmup)
+           if args.backward == "auto" and w.dtype == "bf16" else None)
     cpu = cpu_baseline(w, args.variant, args.cpu_budget) if args.cpu_budget > 0 else None
     gemm = gemm_context(torch) if args.cpu_budget > 0 else None
     v = w.variant(args.variant)
@@ -222,6 +271,7 @@ def main():
                             "sqa_speedup": round(c["sqa_speedup"], 3), "ideal_speedup": c["ideal_speedup"]}
                         for k, c in comps.items()},
         "roofline": roofline,
+        "backward": bwd,
         "cpu_baseline": cpu,
         "pages_claim": "SQA abstract: up to 3x throughput on 32k-200k sequences; hardware not named",
         "context_library_gemm": gemm,
