@@ -8,17 +8,25 @@ The 200k case also multiplies 1% of the key positions by 8 so that some
 softmax rows are sharply peaked.
 
 Seeds: 0x5A510000 + 16 * config_number + variant_index.
-Streams: q = 0, k = 1, v = 2, key-position selection = 3.
+Streams: q = 0, k = 1, v = 2, key-position selection = 3, cache lengths = 4.
+
+Decode workloads (one new token per sequence against its key/value cache)
+take their head shapes from the GQA explainer's KV-cache table (32 query
+heads with 8 K/V groups as in Llama 3 8B, MHA with 32, MQA with 1; d_h = 128)
+and its note that GQA-8 brings 128K-token contexts within reach; the SQA
+variant halves the query heads at the same 8 K/V groups.  Cache lengths are a
+seeded mix shared by all variants of a workload (seed of its first variant):
+sequence 0 fills the cache, the others are uniform in [S_max/4, S_max].
 """
 import math
 from dataclasses import dataclass, field
 
 import numpy as np
 
-from . import normal, scale_positions_bf16, select_positions
+from . import normal, scale_positions_bf16, select_positions, uniform
 
 SEED_BASE = 0x5A510000
-STREAM_Q, STREAM_K, STREAM_V, STREAM_SEL = 0, 1, 2, 3
+STREAM_Q, STREAM_K, STREAM_V, STREAM_SEL, STREAM_LEN = 0, 1, 2, 3, 4
 
 
 @dataclass(frozen=True)
@@ -95,3 +103,68 @@ def make_inputs(workload, variant_name, S=None, B=None):
         scale_positions_bf16(k, peaked, w.peaked_factor)
     return q, k, vv, peaked
 
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    number: int
+    name: str
+    B: int
+    S_max: int
+    d: int
+    mul: float
+    variants: tuple
+    min_len_frac: float = 0.25
+    dtype: str = "bf16"
+
+    @property
+    def scale(self):
+        return 1.0 / math.sqrt(self.d)
+
+    def variant(self, name):
+        for v in self.variants:
+            if v.name == name:
+                return v
+        raise KeyError(name)
+
+    def seed(self, variant_name):
+        idx = [v.name for v in self.variants].index(variant_name)
+        return SEED_BASE + 16 * self.number + idx
+
+
+DECODE_WORKLOADS = {
+    "decode_s128k": DecodeWorkload(6, "decode_s128k", B=4, S_max=131072, d=128, mul=0.5,
+                                   variants=(Variant("gqa", 32, 8), Variant("mha", 32, 32),
+                                             Variant("mqa", 32, 1), Variant("sqa", 16, 8))),
+}
+
+
+def decode_lengths(seed, B, S_max, min_len_frac):
+    """Cache length per sequence: sequence 0 is full, the others uniform
+    integers in [ceil(min_len_frac * S_max), S_max] from stream 4."""
+    lo = max(1, int(math.ceil(min_len_frac * S_max)))
+    lens = np.empty(B, dtype=np.int64)
+    for b in range(B):
+        if b == 0:
+            lens[b] = S_max
+        else:
+            u = uniform(seed, STREAM_LEN, b)          # in (0, 1]
+            lens[b] = min(S_max, lo + int(math.floor(u * (S_max - lo + 1))))
+    return lens
+
+
+def make_decode_inputs(workload, variant_name, S_max=None, B=None):
+    """Host arrays for one decode variant: q [B, H_q, d], k and v caches
+    [B, S_max, H_kv, d] (bf16 bits), and the int64 cache lengths [B].
+    Cache positions at or past a sequence's length hold values too (as a
+    reused cache buffer would); they must not affect the result."""
+    w = workload
+    v = w.variant(variant_name)
+    S_max = w.S_max if S_max is None else S_max
+    B = w.B if B is None else B
+    seed = w.seed(variant_name)
+    q = normal(seed, STREAM_Q, (B, v.H_q, w.d), w.dtype, w.mul)
+    k = normal(seed, STREAM_K, (B, S_max, v.H_kv, w.d), w.dtype, w.mul)
+    vv = normal(seed, STREAM_V, (B, S_max, v.H_kv, w.d), w.dtype, w.mul)
+    lens = decode_lengths(w.seed(w.variants[0].name), B, S_max, w.min_len_frac)
+    return q, k, vv, lens

@@ -44,6 +44,9 @@ def _load():
         lib.sqa_oracle_bwd_dq_rows.restype = ctypes.c_int
         lib.sqa_oracle_bwd_dq_rows.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp, i64, i64, i32, i32, i32,
                                                ctypes.c_double, ctypes.c_int, vp, i64, ctypes.c_int]
+        lib.sqa_oracle_decode.restype = ctypes.c_int
+        lib.sqa_oracle_decode.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, i64, i64, i32, i32, i32,
+                                          ctypes.c_double, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -157,3 +160,38 @@ def attention_grad_dq_rows(q, k, v, dout, scale, rows, causal=False, n_threads=0
     if rc != 0:
         raise MemoryError("oracle: allocation failed")
     return out
+
+
+def decode(q, k, v, scale, seqlens=None, n_threads=0):
+    """fp64 attention of one query token per sequence against its K/V cache.
+
+    q: [B, H_q, d]; k, v: [B, S_max, H_kv, d]; one dtype among uint16 (bf16
+    bits), float32, float64.  seqlens: per-sequence valid cache length
+    (None = S_max); lengths above S_max count as S_max, lengths <= 0 give
+    out = 0 and lse = -inf.  Returns (out [B, H_q, d], lse [B, H_q]), float64.
+    """
+    arrs = [np.ascontiguousarray(a) for a in (q, k, v)]
+    q, k, v = arrs
+    if len({a.dtype for a in arrs}) != 1 or q.dtype not in _DTYPE_CODE:
+        raise TypeError("q, k, v must share one dtype among uint16(bf16 bits), float32, float64")
+    if q.ndim != 3 or k.ndim != 4 or v.shape != k.shape:
+        raise ValueError(f"expected q [B,H_q,d] and k, v [B,S_max,H_kv,d]; got q{q.shape} k{k.shape} v{v.shape}")
+    B, H_q, d = q.shape
+    S_max, H_kv = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape}")
+    lens = None
+    if seqlens is not None:
+        lens = np.ascontiguousarray(seqlens, dtype=np.int64)
+        if lens.shape != (B,):
+            raise ValueError("seqlens must have one entry per sequence")
+    out = np.zeros((B, H_q, d), dtype=np.float64)
+    lse_out = np.zeros((B, H_q), dtype=np.float64)
+    ptr = lambda a: ctypes.c_void_p(a.ctypes.data)
+    rc = _load().sqa_oracle_decode(ptr(q), ptr(k), ptr(v), _DTYPE_CODE[q.dtype], ptr(lens) if lens is not None else None,
+                                   ptr(out), ptr(lse_out), B, S_max, H_q, H_kv, d, float(scale), int(n_threads))
+    if rc == -1:
+        raise ValueError("oracle: invalid arguments")
+    if rc != 0:
+        raise MemoryError("oracle: allocation failed")
+    return out, lse_out

@@ -407,3 +407,88 @@ int sqa_oracle_bwd_dq_rows(const void* q, const void* k, const void* v, const vo
   }
   return failed ? -2 : 0;
 }
+
+/*
+ * Decode: one new query token per sequence against that sequence's
+ * key/value cache.  The GQA explainer's background section puts the cache
+ * at the centre of inference cost (2*G*d_h values stored per token, read in
+ * full for every generated token); the SQA abstract contrasts this
+ * bandwidth-bound regime with its compute-bound one.  The result is the
+ * ordinary attention of a single query row:
+ *
+ *   q    [B, H_q, d]          the token's query heads
+ *   k, v [B, S_max, H_kv, d]  the cache, BSHD, positions 0 .. len_b-1 valid
+ *   seqlens[b]                valid cache length of sequence b (host array;
+ *                             NULL = S_max for every sequence)
+ *   out  [B, H_q, d] fp64,  lse [B, H_q] fp64 (nullable)
+ *
+ *   o[b,h] = sum_{j < len_b} softmax_j(scale * <q[b,h], k[b,j,g]>) v[b,j,g],
+ *   lse[b,h] = log sum_{j < len_b} exp(scale * <q[b,h], k[b,j,g]>),
+ *   g = floor(h / R) as in the forward.
+ *
+ * This is the causal forward's row len_b - 1 when the token sits at that
+ * position (it sees every cached key up to and including its own).
+ * Readings where the pages say nothing: len_b > S_max is taken as S_max; an
+ * empty cache (len_b <= 0) gives the empty sum: o = 0 and lse = -inf.
+ */
+int sqa_oracle_decode(const void* q, const void* k, const void* v, int dtype, const int64_t* seqlens, double* out,
+                      double* lse_out, int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d, double scale,
+                      int n_threads) {
+  if (B < 0 || S_max < 0 || H_q < 1 || H_kv < 1 || d < 1 || H_q % H_kv != 0) return -1;
+  if (dtype < 0 || dtype > 2) return -1;
+  const int64_t items = B * (int64_t)H_q;
+  if (items == 0) return 0;
+  const int32_t R = H_q / H_kv;
+  int failed = 0;
+#ifdef _OPENMP
+  if (n_threads <= 0) n_threads = omp_get_max_threads();
+#else
+  n_threads = 1;
+#endif
+#pragma omp parallel num_threads(n_threads)
+  {
+    double* p = (double*)malloc((size_t)(S_max > 0 ? S_max : 1) * sizeof(double));
+    double* acc = (double*)malloc((size_t)d * sizeof(double));
+    if (!p || !acc) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < items; ++t) {
+      if (!p || !acc) continue;
+      const int64_t b = t / H_q;
+      const int32_t h = (int32_t)(t % H_q);
+      const int32_t g = h / R;
+      int64_t len = seqlens ? seqlens[b] : S_max;
+      if (len > S_max) len = S_max;
+      double* o = out + t * (int64_t)d;
+      if (len <= 0) {
+        for (int32_t e = 0; e < d; ++e) o[e] = 0.0;
+        if (lse_out) lse_out[t] = -INFINITY;
+        continue;
+      }
+      const int64_t q_off = t * (int64_t)d;
+      double m = -INFINITY;
+      for (int64_t j = 0; j < len; ++j) {
+        const int64_t k_off = ((b * S_max + j) * H_kv + g) * (int64_t)d;
+        double dot = 0.0;
+        for (int32_t e = 0; e < d; ++e) dot += load_elem(q, dtype, q_off + e) * load_elem(k, dtype, k_off + e);
+        p[j] = scale * dot;
+        if (p[j] > m) m = p[j];
+      }
+      double l = 0.0;
+      for (int32_t e = 0; e < d; ++e) acc[e] = 0.0;
+      for (int64_t j = 0; j < len; ++j) {
+        const double a = exp(p[j] - m);
+        l += a;
+        const int64_t v_off = ((b * S_max + j) * H_kv + g) * (int64_t)d;
+        for (int32_t e = 0; e < d; ++e) acc[e] += a * load_elem(v, dtype, v_off + e);
+      }
+      for (int32_t e = 0; e < d; ++e) o[e] = acc[e] / l;
+      if (lse_out) lse_out[t] = m + log(l);
+    }
+    free(p);
+    free(acc);
+  }
+  return failed ? -2 : 0;
+}

@@ -66,3 +66,19 @@ def test_workload_shapes():
     assert [(v.H_q, v.H_kv) for v in w.variants] == [(16, 16), (16, 4), (8, 4), (4, 4)]
     q, k, v, _ = make_inputs(w, "sqa", S=64)
     assert q.shape == (2, 64, 8, 64) and k.shape == (2, 64, 4, 64) and q.dtype == np.uint16
+
+
+def test_decode_lengths_recipe():
+    from inputs.configs import DECODE_WORKLOADS, decode_lengths, make_decode_inputs
+    w = DECODE_WORKLOADS["decode_s128k"]
+    lens = decode_lengths(w.seed(w.variants[0].name), w.B, w.S_max, w.min_len_frac)
+    assert lens[0] == w.S_max
+    assert (lens >= w.S_max // 4).all() and (lens <= w.S_max).all()
+    # same lengths for every variant of the workload, deterministic
+    for v in w.variants:
+        q, k, vv, l2 = make_decode_inputs(w, v.name, S_max=256)
+        assert q.shape == (w.B, v.H_q, w.d) and k.shape == (w.B, 256, v.H_kv, w.d) == vv.shape
+        np.testing.assert_array_equal(l2, decode_lengths(w.seed(w.variants[0].name), w.B, 256, w.min_len_frac))
+    # a long uniform sample spans the range
+    many = decode_lengths(123, 2000, 1000, 0.25)
+    assert many.min() <= 260 and many[1:].max() >= 990 and many[1:].min() >= 250

@@ -435,3 +435,99 @@ def test_grad_dq_rows_equal_full_gradient_rows():
         dq, _, _ = oracle.attention_grad(q, k, v, dout, 0.45, causal=causal)
         sub = oracle.attention_grad_dq_rows(q, k, v, dout, 0.45, rows, causal=causal)
         np.testing.assert_allclose(sub, dq[:, rows], rtol=1e-14, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# decode: one query token against a key/value cache of per-sequence length
+
+
+def _decode_case(seed, B, S_max, H_q, H_kv, d):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, H_q, d)), rng.standard_normal((B, S_max, H_kv, d)),
+            rng.standard_normal((B, S_max, H_kv, d)))
+
+
+def test_decode_equals_causal_forward_row():
+    """The token at position len-1 of a causal forward sees exactly the cache
+    prefix 0..len-1: decode must equal that row of the (separately pinned)
+    forward oracle, output and log-normaliser."""
+    B, S_max, H_q, H_kv, d = 3, 37, 8, 2, 16
+    q, k, v = _decode_case(11, B, S_max, H_q, H_kv, d)
+    lens = np.array([37, 1, 20])
+    out, lse = oracle.decode(q, k, v, 0.3, seqlens=lens)
+    rng = np.random.default_rng(12)
+    for b, n in enumerate(lens):
+        qf = rng.standard_normal((1, n, H_q, d))
+        qf[0, n - 1] = q[b]
+        kk, vv = np.ascontiguousarray(k[b:b + 1, :n]), np.ascontiguousarray(v[b:b + 1, :n])
+        row = oracle.attention(qf, kk, vv, 0.3, causal=True, rows=[n - 1])
+        np.testing.assert_allclose(out[b], row[0, 0], rtol=1e-12, atol=1e-13)
+        lrow = oracle.lse(qf, kk, 0.3, causal=True, rows=[n - 1])
+        np.testing.assert_allclose(lse[b], lrow[0, 0], rtol=1e-12, atol=1e-13)
+
+
+def test_decode_matches_torch_sdpa_with_length_mask():
+    B, S_max, H_q, H_kv, d = 4, 29, 6, 3, 8
+    q, k, v = _decode_case(13, B, S_max, H_q, H_kv, d)
+    lens = np.array([29, 5, 17, 2])
+    out, lse = oracle.decode(q, k, v, 0.41, seqlens=lens)
+    R = H_q // H_kv
+    tq = torch.from_numpy(q)[:, :, None, :]                                     # [B, H_q, 1, d]
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(R, dim=1)   # [B, H_q, S, d]
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(R, dim=1)
+    mask = (torch.arange(S_max)[None, :] < torch.from_numpy(lens)[:, None])[:, None, None, :]
+    ref = torch.nn.functional.scaled_dot_product_attention(tq.contiguous(), tk.contiguous(), tv.contiguous(),
+                                                           attn_mask=mask, scale=0.41)[:, :, 0, :]
+    np.testing.assert_allclose(out, ref.numpy(), rtol=1e-12, atol=1e-13)
+    scores = 0.41 * (tq @ tk.transpose(-1, -2))[:, :, 0, :]
+    scores = scores.masked_fill(~mask[:, :, 0, :], float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(scores, dim=-1).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_decode_closed_forms():
+    B, S_max, H_q, H_kv, d = 3, 16, 4, 2, 8
+    _, k, v = _decode_case(14, B, S_max, H_q, H_kv, d)
+    lens = np.array([16, 1, 0])
+    out, lse = oracle.decode(np.zeros((B, H_q, d)), k, v, 0.5, seqlens=lens)
+    for h in range(H_q):
+        g = h // (H_q // H_kv)
+        # constant scores: the mean of the valid values, lse = log(len)
+        np.testing.assert_allclose(out[0, h], v[0, :16, g].mean(axis=0), rtol=1e-13, atol=1e-14)
+        assert abs(lse[0, h] - math.log(16)) < 1e-13
+        # one valid key: its value, lse = its score (0 here)
+        np.testing.assert_array_equal(out[1, h], v[1, 0, g])
+        assert lse[1, h] == 0.0
+        # empty cache: the empty sum
+        np.testing.assert_array_equal(out[2, h], np.zeros(d))
+        assert lse[2, h] == -math.inf
+
+
+def test_decode_length_above_cache_is_clamped_and_default_is_full():
+    q, k, v = _decode_case(15, 2, 12, 4, 4, 8)
+    a = oracle.decode(q, k, v, 0.2, seqlens=[12, 12])
+    b = oracle.decode(q, k, v, 0.2, seqlens=[40, 1 << 40])
+    c = oracle.decode(q, k, v, 0.2)
+    for x, y in ((a, b), (a, c)):
+        np.testing.assert_array_equal(x[0], y[0])
+        np.testing.assert_array_equal(x[1], y[1])
+
+
+def test_decode_grouped_equals_mha_on_repeated_cache():
+    q, k, v = _decode_case(16, 2, 21, 8, 2, 8)
+    lens = [21, 9]
+    a = oracle.decode(q, k, v, 0.3, seqlens=lens)
+    b = oracle.decode(q, np.repeat(k, 4, axis=2), np.repeat(v, 4, axis=2), 0.3, seqlens=lens)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_decode_bf16_inputs_decode_exactly():
+    seed = 17
+    q = inputs.normal(seed, 0, (2, 4, 32), "bf16", 0.5)
+    k = inputs.normal(seed, 1, (2, 50, 2, 32), "bf16", 0.5)
+    v = inputs.normal(seed, 2, (2, 50, 2, 32), "bf16", 0.5)
+    f = lambda a: inputs.bf16_bits_to_f32(a).astype(np.float64)
+    a = oracle.decode(q, k, v, 0.17, seqlens=[50, 31])
+    b = oracle.decode(f(q), f(k), f(v), 0.17, seqlens=[50, 31])
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
