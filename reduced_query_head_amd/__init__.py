@@ -1,4 +1,5 @@
-"""Python binding of libsqa: decoupled-head attention forward on MI355X.
+"""Python binding of libsqa: decoupled-head attention on MI355X (forward,
+backward, decode).
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``lib/libsqa.so`` (sources in ``csrc/``, C-ABI in
@@ -44,6 +45,11 @@ def load_library(path=None):
                                  ctypes.c_float, ctypes.c_int, vp]
     lib.sqa_attn_bwd_workspace_size.restype = i64
     lib.sqa_attn_bwd_workspace_size.argtypes = [i64, i64, i32]
+    lib.sqa_attn_decode.restype = ctypes.c_int
+    lib.sqa_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, ctypes.c_int,
+                                    ctypes.c_float, vp]
+    lib.sqa_attn_decode_workspace_size.restype = i64
+    lib.sqa_attn_decode_workspace_size.argtypes = [i64, i64, i32, i32, i32]
     lib.sqa_status_string.restype = ctypes.c_char_p
     lib.sqa_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -171,3 +177,67 @@ def attn_bwd(q, k, v, out, dout, lse, scale=None, causal=False, stream=None, dq=
     if st != SQA_OK:
         raise SqaError(st, status_string(st))
     return dq, dk, dv
+
+
+def attn_decode_workspace_size(B, S_max, H_q, H_kv, d):
+    return int(load_library().sqa_attn_decode_workspace_size(B, S_max, H_q, H_kv, d))
+
+
+def attn_decode_raw(q, k_cache, v_cache, seqlens, out, lse, workspace, workspace_bytes, B, S_max, H_q, H_kv, d,
+                    dtype, scale, stream):
+    """Direct call of sqa_attn_decode with integer device addresses; returns the status."""
+    return load_library().sqa_attn_decode(q, k_cache, v_cache, seqlens, out, lse, workspace, workspace_bytes, B,
+                                          S_max, H_q, H_kv, d, dtype, scale, stream)
+
+
+def attn_decode(q, k_cache, v_cache, seqlens=None, out=None, scale=None, stream=None, return_lse=False, lse=None,
+                workspace=None):
+    """One query token per sequence against its key/value cache.
+
+    q: [B, H_q, d] bfloat16; k_cache, v_cache: [B, S_max, H_kv, d] bfloat16;
+    seqlens: int32 [B] GPU tensor of cache lengths (None = S_max).  Returns
+    out [B, H_q, d] (and the fp32 [B, H_q] log-normaliser with return_lse).
+    A uint8 workspace of attn_decode_workspace_size(...) bytes is allocated
+    if none is given.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bfloat16 GPU tensor")
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError(f"expected q [B,H_q,d], caches [B,S_max,H_kv,d]; got q{tuple(q.shape)} "
+                         f"k{tuple(k_cache.shape)} v{tuple(v_cache.shape)}")
+    B, H_q, d = q.shape
+    S_max, H_kv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k_cache.shape)}")
+    if seqlens is not None and (not seqlens.is_cuda or seqlens.dtype != torch.int32 or seqlens.shape != (B,)
+                                or not seqlens.is_contiguous()):
+        raise ValueError("seqlens must be a contiguous int32 GPU tensor of shape [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous GPU tensor shaped and typed like q")
+    if return_lse and lse is None:
+        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H_q) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor of shape [B, H_q]")
+    ws_bytes = attn_decode_workspace_size(B, S_max, H_q, H_kv, d)
+    if ws_bytes < 0:
+        raise ValueError("invalid sizes")
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = attn_decode_raw(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                         seqlens.data_ptr() if seqlens is not None else None, out.data_ptr(),
+                         lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
+                         workspace.numel() * workspace.element_size(), B, S_max, H_q, H_kv, d, SQA_BF16,
+                         float(scale), handle)
+    if st != SQA_OK:
+        raise SqaError(st, status_string(st))
+    return (out, lse) if (return_lse or lse is not None) else out

@@ -5,7 +5,7 @@ import subprocess
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["csrc/api.cpp", "csrc/attn_fwd.hip", "csrc/attn_bwd.hip"]
+SOURCES = ["csrc/api.cpp", "csrc/attn_fwd.hip", "csrc/attn_bwd.hip", "csrc/attn_decode.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
     # no packed-fp32 instructions in device code

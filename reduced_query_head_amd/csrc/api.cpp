@@ -178,3 +178,67 @@ SQA_API sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, con
   a.stream = (void*)stream;
   return sqa::launch_attn_bwd(a) == hipSuccess ? SQA_OK : SQA_ERR_HIP;
 }
+
+SQA_API int64_t sqa_attn_decode_workspace_size(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d) {
+  if (B < 0 || S_max < 0 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || d < 1) return -1;
+  if (S_max > (int64_t)1 << 30 || B > ((int64_t)1 << 31)) return -1;
+  return sqa::decode_plan(B, S_max, H_q, H_kv, d).workspace_bytes;
+}
+
+SQA_API sqa_status sqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
+                                   void* out, float* lse, void* workspace, int64_t workspace_bytes, int64_t B,
+                                   int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d, sqa_dtype dtype,
+                                   float scale, sqa_stream_t stream) {
+  if (B < 0 || S_max < 0 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0) return SQA_ERR_INVALID_ARGUMENT;
+  if (dtype != SQA_BF16 && dtype != SQA_FP32) return SQA_ERR_INVALID_ARGUMENT;
+  if (!isfinite(scale) || d < 1) return SQA_ERR_INVALID_ARGUMENT;
+  if (B == 0) return SQA_OK;
+  if (!q || !out || !workspace || (S_max > 0 && (!k_cache || !v_cache))) return SQA_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out | (uintptr_t)workspace) & 15u)
+    return SQA_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)lse | (uintptr_t)seqlens) & 3u) return SQA_ERR_INVALID_ARGUMENT;
+  if (S_max > (int64_t)1 << 30 || B > ((int64_t)1 << 31)) return SQA_ERR_UNSUPPORTED;
+  const int64_t elem = dtype == SQA_BF16 ? 2 : 4;
+  int64_t q_elems, q_bytes, cache_rows, kv_elems, kv_bytes, lse_bytes;
+  if (!mul_ok(B, (int64_t)H_q * d, &q_elems) || !mul_ok(q_elems, elem, &q_bytes) ||
+      !mul_ok(B, S_max, &cache_rows) || !mul_ok(cache_rows, (int64_t)H_kv * d, &kv_elems) ||
+      !mul_ok(kv_elems, elem, &kv_bytes) || !mul_ok(B, (int64_t)H_q * 4, &lse_bytes))
+    return SQA_ERR_INVALID_ARGUMENT;
+  const sqa::DecodePlan plan = sqa::decode_plan(B, S_max, H_q, H_kv, d);
+  if (workspace_bytes < plan.workspace_bytes) return SQA_ERR_INVALID_ARGUMENT;
+  const void* ins[4] = {q, k_cache, v_cache, seqlens};
+  const int64_t in_bytes[4] = {q_bytes, kv_bytes, kv_bytes, seqlens ? B * 4 : 0};
+  const void* outs[3] = {out, lse, workspace};
+  const int64_t out_bytes[3] = {q_bytes, lse ? lse_bytes : 0, plan.workspace_bytes};
+  for (int i = 0; i < 3; ++i) {
+    if (!outs[i]) continue;
+    for (int j = 0; j < 4; ++j)
+      if (ins[j] && ranges_overlap(outs[i], out_bytes[i], ins[j], in_bytes[j])) return SQA_ERR_INVALID_ARGUMENT;
+    for (int j = i + 1; j < 3; ++j)
+      if (outs[j] && ranges_overlap(outs[i], out_bytes[i], outs[j], out_bytes[j])) return SQA_ERR_INVALID_ARGUMENT;
+  }
+  if (dtype != SQA_BF16) return SQA_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64 && d != 128) return SQA_ERR_UNSUPPORTED;
+  if ((plan.n_waves + 3) / 4 > INT32_MAX || (B * H_q + 3) / 4 > INT32_MAX) return SQA_ERR_UNSUPPORTED;
+
+  sqa::DecodeArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.seqlens = seqlens;
+  a.out = out;
+  a.lse = lse;
+  a.workspace = workspace;
+  a.B = B;
+  a.S_max = S_max;
+  a.H_q = H_q;
+  a.H_kv = H_kv;
+  a.d = d;
+  const float log2e = 1.4426950408889634f;
+  const float mag = fabsf(scale);
+  a.c = mag > 0.f ? mag * log2e : 1e-30f;
+  if (!isfinite(a.c)) return SQA_ERR_INVALID_ARGUMENT;
+  a.negate_q = scale < 0.f;
+  a.stream = (void*)stream;
+  return sqa::launch_attn_decode(a) == hipSuccess ? SQA_OK : SQA_ERR_HIP;
+}

@@ -56,6 +56,36 @@ int64_t bwd_workspace_bytes(int64_t B, int64_t S, int32_t H_q);
 int64_t bwd_grid_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv);
 int64_t bf16_grid_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv);
 
+struct DecodeArgs {
+  const void* q;          // [B, H_q, d]
+  const void* k;          // [B, S_max, H_kv, d]
+  const void* v;
+  const int32_t* seqlens; // [B] device array, or null (= S_max)
+  void* out;              // [B, H_q, d]
+  float* lse;             // [B, H_q] or null
+  void* workspace;        // decode_plan(...).workspace_bytes bytes
+  int64_t B;
+  int64_t S_max;
+  int32_t H_q;
+  int32_t H_kv;
+  int32_t d;
+  float c;                // |scale| * log2(e), or a tiny positive value when scale == 0
+  bool negate_q;          // scale < 0
+  void* stream;
+};
+
+struct DecodePlan {
+  int head_blocks;        // ceil(R / 32)
+  int n_splits;
+  int split_len;          // keys per split
+  int64_t n_waves;
+  int64_t part_o_bytes;
+  int64_t workspace_bytes;
+};
+
+DecodePlan decode_plan(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d);
+hipError_t launch_attn_decode(const DecodeArgs& a);
+
 }  // namespace sqa
 
 #endif

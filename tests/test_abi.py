@@ -122,3 +122,54 @@ def test_bwd_invalid(kw):
 def test_bwd_unsupported_and_empty():
     assert _call_bwd(d=80) == sqa.SQA_ERR_UNSUPPORTED
     assert _call_bwd(B=0, q=0, k=0, v=0, out=0, dout=0, lse=0, dq=0, dk=0, dv=0, ws=0, ws_bytes=0) == sqa.SQA_OK
+
+
+G = 1 << 30
+
+
+def _call_dec(**kw):
+    a = dict(q=FAKE, k=FAKE + G, v=FAKE + 2 * G, seqlens=FAKE + 3 * G, out=FAKE + 4 * G, lse=FAKE + 5 * G,
+             ws=FAKE + 6 * G, ws_bytes=None, B=4, S_max=4096, H_q=32, H_kv=8, d=128, dtype=0, scale=0.088)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = max(0, sqa.attn_decode_workspace_size(a["B"], a["S_max"], a["H_q"], a["H_kv"], a["d"]))
+    return sqa.attn_decode_raw(a["q"], a["k"], a["v"], a["seqlens"], a["out"], a["lse"], a["ws"], a["ws_bytes"],
+                               a["B"], a["S_max"], a["H_q"], a["H_kv"], a["d"], a["dtype"], a["scale"], 0)
+
+
+def test_decode_workspace_size():
+    n = sqa.attn_decode_workspace_size(4, 4096, 32, 8, 128)
+    assert n > 0 and n % 16 == 0
+    # partials of every query head of every split: at least one (d + 2) fp32 record per head
+    assert n >= 4 * 32 * (128 + 2) * 4
+    assert sqa.attn_decode_workspace_size(4, 0, 32, 8, 128) > 0
+    for bad in [(-1, 10, 4, 2, 64), (1, -1, 4, 2, 64), (1, 10, 0, 1, 64), (1, 10, 6, 4, 64), (1, 10, 4, 2, 0),
+                (1, (1 << 30) + 1, 4, 2, 64)]:
+        assert sqa.attn_decode_workspace_size(*bad) == -1
+
+
+@pytest.mark.parametrize("kw", [
+    dict(H_q=6, H_kv=4), dict(H_q=2, H_kv=4), dict(H_q=0), dict(B=-1), dict(S_max=-1), dict(d=0),
+    dict(dtype=5), dict(scale=float("nan")), dict(scale=float("-inf")), dict(scale=-3e38),
+    dict(q=0), dict(k=0), dict(v=0), dict(out=0), dict(ws=0),
+    dict(q=FAKE + 8), dict(out=FAKE + 4 * G + 4), dict(ws=FAKE + 6 * G + 2), dict(lse=FAKE + 5 * G + 2),
+    dict(seqlens=FAKE + 3 * G + 1),
+    dict(ws_bytes=16),                         # workspace too small
+    dict(out=FAKE + 64),                       # out overlaps q
+    dict(ws=FAKE + G + 4096),                  # workspace overlaps the k cache
+    dict(lse=FAKE + 4 * G + 256),              # lse overlaps out
+    dict(out=FAKE + 3 * G),                    # out overlaps seqlens
+])
+def test_decode_invalid(kw):
+    assert _call_dec(**kw) == sqa.SQA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(dtype=1), dict(d=96), dict(d=16), dict(d=256)])
+def test_decode_unsupported(kw):
+    assert _call_dec(**kw) == sqa.SQA_ERR_UNSUPPORTED
+
+
+def test_decode_empty_and_optional_pointers():
+    assert _call_dec(B=0, q=0, k=0, v=0, out=0, ws=0) == sqa.SQA_OK
+    # seqlens and lse are optional; they still may not be misaligned (checked above)
+    assert _call_dec(B=0, seqlens=0, lse=0) == sqa.SQA_OK
