@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_BYTES_PER_S = 8.0e12
 KERNEL_SOURCES = ["reduced_query_head_amd/csrc/attn_fwd.hip", "reduced_query_head_amd/csrc/device_common.h"]
 
 
@@ -130,6 +131,52 @@ def time_backward(sqa, torch, w, variant, steps, warmup):
             "kernels": "bwd_stats_bf16 + bwd_dq_bf16 + bwd_dkdv_bf16 (one sqa_attn_bwd call)"}
 
 
+def time_decode(sqa, torch, wname, steps, warmup):
+    """Decode (one token per sequence against its K/V cache) for every head
+    configuration of the decode workload, on the same cache lengths.
+    Algorithmic bytes per call: the valid part of the K and V caches
+    (sum_b len_b * H_kv * d * 2 tensors * 2 bytes) plus q, out and lse; the
+    call is bound by HBM bandwidth (8 TB/s)."""
+    from inputs.configs import DECODE_WORKLOADS, decode_lengths, make_decode_inputs
+    w = DECODE_WORKLOADS[wname]
+    res = {}
+    for var in w.variants:
+        q, k, v, lens = make_decode_inputs(w, var.name)
+        dq_, dk_, dv_ = (torch.from_numpy(a).view(torch.bfloat16).to("cuda") for a in (q, k, v))
+        dl = torch.from_numpy(lens.astype("int32")).to("cuda")
+        del q, k, v
+        out = torch.empty_like(dq_)
+        lse = torch.empty((w.B, var.H_q), dtype=torch.float32, device="cuda")
+        ws = torch.empty(sqa.attn_decode_workspace_size(w.B, w.S_max, var.H_q, var.H_kv, w.d), dtype=torch.uint8,
+                         device="cuda")
+        stream = torch.cuda.current_stream()
+
+        def run():
+            sqa.attn_decode(dq_, dk_, dv_, seqlens=dl, out=out, lse=lse, scale=w.scale, stream=stream, workspace=ws)
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for i in range(steps):
+            run()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        ms = sum(per) / steps
+        nbytes = int(lens.sum()) * var.H_kv * w.d * 2 * 2 + 2 * w.B * var.H_q * w.d * 2 + w.B * var.H_q * 4
+        res[var.name] = {"H_q": var.H_q, "H_kv": var.H_kv, "ms_per_call": round(ms, 4), "min_ms": round(min(per), 4),
+                         "bytes_per_call": nbytes, "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                         "frac_hbm_peak": round(nbytes / (ms * 1e-3) / PEAK_HBM_BYTES_PER_S, 4),
+                         "tokens_per_s": round(w.B / (ms * 1e-3), 1)}
+        del dq_, dk_, dv_, dl, out, lse, ws
+        torch.cuda.empty_cache()
+    return {"workload": w.name, "B": w.B, "S_max": w.S_max, "d": w.d,
+            "cache_lengths": [int(x) for x in decode_lengths(w.seed(w.variants[0].name), w.B, w.S_max,
+                                                             w.min_len_frac)], "variants": res,
+            "kernels": "attn_decode_split_bf16 + attn_decode_combine_bf16 (one sqa_attn_decode call)"}
+
+
 def gemm_context(torch, n=8192, iters=10):
     """A plain bf16 GEMM from the vendor library on random N(0,1) data, as a
     practical reference for dense bf16 throughput on this GPU (the chip is
@@ -195,6 +242,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0 = skip)")
     ap.add_argument("--backward", choices=["auto", "none", "only"], default="auto",
                     help="time the backward too (auto: bf16 workloads), or only it")
+    ap.add_argument("--decode", choices=["auto", "none", "only"], default="auto",
+                    help="time the decode workload too (auto), or only it")
+    ap.add_argument("--decode-workload", default="decode_s128k")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -224,6 +274,10 @@ def main():
 
     w = WORKLOADS[args.workload]
     sqa.load_library()
+    if args.decode == "only":
+        print(json.dumps({"decode": time_decode(sqa, torch, args.decode_workload, args.steps, args.warmup)}),
+              flush=True)
+        return
     if args.backward == "only":
         print(json.dumps({"backward": time_backward(sqa, torch, w, args.variant, args.steps, args.warmup)}),
               flush=True)
@@ -245,6 +299,7 @@ def main():
                 "flops_per_launch": main_res["flops"], "avg_launch_ms": round(main_res["avg_launch_ms"], 4)}
     bwd = (time_backward(sqa, torch, w, args.variant, max(3, args.steps // 2), args.warmup)
            if args.backward == "auto" and w.dtype == "bf16" else None)
+    dec = time_decode(sqa, torch, args.decode_workload, 20, 3) if args.decode == "auto" else None
     cpu = cpu_baseline(w, args.variant, args.cpu_budget) if args.cpu_budget > 0 else None
     gemm = gemm_context(torch) if args.cpu_budget > 0 else None
     v = w.variant(args.variant)
@@ -272,6 +327,7 @@ def main():
                         for k, c in comps.items()},
         "roofline": roofline,
         "backward": bwd,
+        "decode": dec,
         "cpu_baseline": cpu,
         "pages_claim": "SQA abstract: up to 3x throughput on 32k-200k sequences; hardware not named",
         "context_library_gemm": gemm,

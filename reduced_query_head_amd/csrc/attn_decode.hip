@@ -17,9 +17,11 @@
 //    from HBM into the MFMA's A-operand registers; V goes global -> LDS by
 //    DMA into a wave-private double buffer and is read back transposed
 //    (ds_read_b64_tr_b16) for O^T += V^T P^T, as in the forward.  Waves are
-//    independent (no workgroup barrier).  Each writes the split's running
-//    maximum m (log2 units), row sum l and unnormalised O^T to a workspace.
-//  * attn_decode_combine: one wave per (b, h) merges the splits of that
+//    independent (no workgroup barrier).  K is loaded two blocks ahead and V
+//    one block ahead, so each wave keeps about 24 KiB of cache reads in
+//    flight.  Each writes the split's running maximum m (log2 units), row sum
+//    l and unnormalised O^T to a workspace.
+//  * attn_decode_combine: one workgroup per (b, h) merges the splits of that
 //    head: M = max m_s, L = sum l_s 2^(m_s - M), O = sum O_s 2^(m_s - M) / L,
 //    and writes the bf16 output and lse = ln2 (M + log2 L).
 // Cache lengths come from a device array (or are all S_max); a length above
@@ -76,14 +78,16 @@ __global__ __launch_bounds__(kWavesDec * 64, 2) void attn_decode_split_bf16(Deco
   const int half = lane >> 5;
   const int col = lane & 31;
 
+  // wave -> (b, split, head block, K/V head), K/V head fastest: waves that
+  // run together read all heads of the same cache positions (whole rows)
   const int64_t wid = (int64_t)blockIdx.x * kWavesDec + wave;
   if (wid >= p.n_waves) return;   // wave-uniform; no barrier in this kernel
-  const int split = (int)(wid % p.n_splits);
-  const int64_t unit = wid / p.n_splits;
-  const int hb = (int)(unit % p.HB);
-  const int64_t bg = unit / p.HB;
-  const int g = (int)(bg % p.H_kv);
-  const int b = (int)(bg / p.H_kv);
+  const int g = (int)(wid % p.H_kv);
+  const int64_t r1 = wid / p.H_kv;
+  const int hb = (int)(r1 % p.HB);
+  const int64_t r2 = r1 / p.HB;
+  const int split = (int)(r2 % p.n_splits);
+  const int b = (int)(r2 / p.n_splits);
 
   const int len = cache_len(p, b);
   const int k0 = split * p.split_len;
@@ -107,14 +111,18 @@ __global__ __launch_bounds__(kWavesDec * 64, 2) void attn_decode_split_bf16(Deco
 
   // K rows as the A operand: lane holds key (row0 + col), head dims
   // ks*16 + half*8 ... +7; rows past the split end are clamped (and masked)
-  bf16x8 kf[KS];
-  auto load_k = [&](int row0) {
+  bf16x8 kfa[KS], kfb[KS];   // K of even / odd blocks, loaded two blocks ahead
+  auto load_k = [&](bf16x8 (&dst)[KS], int row0) {
     const int row = min(row0 + col, k1 - 1);
     const uint16_t* kp = k_base + (int64_t)row * kv_stride + half * 8;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const bf16x8*)(kp + ks * 16);
+    for (int ks = 0; ks < KS; ++ks) dst[ks] = *(const bf16x8*)(kp + ks * 16);
   };
-  load_k(k0);
+  // K loads are issued for every step, also past the split end (rows clamped
+  // to the last valid one, cache hits): a fixed pattern of KS loads per step
+  // that the wait counts below rely on
+  load_k(kfa, k0);
+  load_k(kfb, k0 + kBlk);
 
   // Q^T as the B operand: lane holds query head h (column col), same dims
   bf16x8 qf[KS];
@@ -149,22 +157,21 @@ __global__ __launch_bounds__(kWavesDec * 64, 2) void attn_decode_split_bf16(Deco
   const float c = p.c;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  for (int t = 0; t < n_blk; ++t) {
+  // Block t needs V_t (copied in the previous step) and K_t (loaded two steps
+  // earlier).  The only memory operations issued after both are the KS loads
+  // of K_{t+1}: wait until at most those remain.
+  auto step = [&](int t, bf16x8 (&kf)[KS], SQA_LDS uint16_t* vt, SQA_LDS uint16_t* vnext) {
     const int r0 = k0 + t * kBlk;
-    SQA_LDS uint16_t* vt = (t & 1) ? vbuf1 : vbuf0;
-    wait_copies();   // this block's V copies (and K loads) have landed
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KS) : "memory");
 
     // S^T = K Q^T: 32 keys x 32 query heads
     f32x16 s = (f32x16){};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
 
-    // next block in flight while this one finishes
-    if (t + 1 < n_blk) {
-      cp.issue(v_base + (int64_t)(r0 + kBlk) * kv_stride, kv_stride, k1 - r0 - kBlk, (t & 1) ? vbuf0 : vbuf1, 0);
-      load_k(r0 + kBlk);
-    }
-
+    // V of the next block and K of the block after it in flight
+    if (t + 1 < n_blk) cp.issue(v_base + (int64_t)(r0 + kBlk) * kv_stride, kv_stride, k1 - r0 - kBlk, vnext, 0);
+    load_k(kf, r0 + 2 * kBlk);
     // keys past the split end: s[r] holds key r0 + 8*(r/4) + 4*half + r%4
     if (r0 + kBlk > k1) {
       const int lim = k1 - 1 - r0 - 4 * half;
@@ -211,7 +218,12 @@ __global__ __launch_bounds__(kWavesDec * 64, 2) void attn_decode_split_bf16(Deco
       }
     }
     l_run += psum;
+  };
+  for (int t = 0; t < n_blk; t += 2) {
+    step(t, kfa, vbuf0, vbuf1);
+    if (t + 1 < n_blk) step(t + 1, kfb, vbuf1, vbuf0);
   }
+  wait_copies();   // no load outlives the loop
 
   const float l_tot = wave_pair_sum(l_run);
   if (!valid) return;
@@ -227,47 +239,70 @@ __global__ __launch_bounds__(kWavesDec * 64, 2) void attn_decode_split_bf16(Deco
           (f32x4){o[db][4 * j], o[db][4 * j + 1], o[db][4 * j + 2], o[db][4 * j + 3]};
 }
 
-// One wave per (b, h): merge the non-empty splits of that head.
+// One workgroup per (b, h): merge the non-empty splits of that head.  The
+// 256 threads form SG split groups of D/4 lanes, each lane holding 4 head
+// dims (16-byte loads); a maximum pass over the splits, a weighted-sum pass,
+// then an LDS reduction over the split groups.
 template <int D>
-__global__ __launch_bounds__(256) void attn_decode_combine_bf16(DecodeParams p, int64_t rows) {
-  constexpr int PER = (D + 63) / 64;   // head dims per lane
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // b * H_q + h
-  if (row >= rows) return;
+__global__ __launch_bounds__(256) void attn_decode_combine_bf16(DecodeParams p) {
+  constexpr int LANES = D / 4;          // lanes per split group
+  constexpr int SG = 256 / LANES;       // split groups
+  __shared__ float red_m[4];
+  __shared__ float red_l[SG];
+  __shared__ f32x4 red_o[SG][LANES];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int grp = tid / LANES;
+  const int dl = tid % LANES;
+  const int64_t row = blockIdx.x;      // b * H_q + h
   const int b = (int)(row / p.H_q);
   const int len = cache_len(p, b);
   uint16_t* op = p.out + row * D;
-  if (len <= 0) {
-#pragma unroll
-    for (int e = 0; e < PER; ++e)
-      if (lane * PER + e < D) op[lane * PER + e] = 0;
-    if (p.lse && lane == 0) p.lse[row] = -__builtin_inff();
+  if (len <= 0) {   // uniform over the workgroup
+    if (tid < D) op[tid] = 0;
+    if (p.lse && tid == 0) p.lse[row] = -__builtin_inff();
     return;
   }
   const int n_valid = (len + p.split_len - 1) / p.split_len;
   const float* ml = p.part_ml + row * p.n_splits * 2;
-  float M = -__builtin_inff();
-  for (int s = 0; s < n_valid; ++s) M = fmaxf(M, ml[2 * s]);
-  float L = 0.f;
-  float acc[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   const float* po = p.part_o + row * p.n_splits * D;
-  for (int s = 0; s < n_valid; ++s) {
-    const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
-    L += w * ml[2 * s + 1];
+
+  float M = -__builtin_inff();
+  for (int s = tid; s < n_valid; s += 256) M = fmaxf(M, ml[2 * s]);
 #pragma unroll
-    for (int e = 0; e < PER; ++e)
-      if (lane * PER + e < D) acc[e] += w * po[(int64_t)s * D + lane * PER + e];
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) red_m[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+
+  float L = 0.f;
+  f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = grp; s < n_valid; s += SG) {
+    const float2 mls = *(const float2*)(ml + 2 * s);
+    const float w = __builtin_amdgcn_exp2f(mls.x - M);
+    L += w * mls.y;
+    acc += w * *(const f32x4*)(po + (int64_t)s * D + dl * 4);
   }
-  const float inv = 1.0f / L;
+  red_o[grp][dl] = acc;
+  if (dl == 0) red_l[grp] = L;
+  __syncthreads();
+  if (tid < LANES) {
+    float Lt = 0.f;
+    f32x4 o = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int e = 0; e < PER; ++e)
-    if (lane * PER + e < D) {
-      const __bf16 r = (__bf16)(acc[e] * inv);
-      op[lane * PER + e] = __builtin_bit_cast(uint16_t, r);
+    for (int g2 = 0; g2 < SG; ++g2) {
+      Lt += red_l[g2];
+      o += red_o[g2][tid];
     }
-  if (p.lse && lane == 0) p.lse[row] = (M + log2f(L)) * 0.69314718055994531f;
+    const float inv = 1.0f / Lt;
+    bf16x4 w4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w4[e] = (__bf16)(o[e] * inv);
+    *(bf16x4*)(op + tid * 4) = w4;
+    if (p.lse && tid == 0) p.lse[row] = (M + log2f(Lt)) * 0.69314718055994531f;
+  }
 }
 
 template <int D>
@@ -297,25 +332,27 @@ hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& plan) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = a.B * a.H_q;
-  hipLaunchKernelGGL((attn_decode_combine_bf16<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
-                     (hipStream_t)a.stream, p, rows);
+  hipLaunchKernelGGL((attn_decode_combine_bf16<D>), dim3((unsigned)rows), dim3(256), 0, (hipStream_t)a.stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Split plan: enough waves to keep every CU's 8 wave slots busy a few times
-// over, each split at least 64 keys (two blocks) long.
+// Split plan: about 8 waves per wave slot of the chip (8 per CU), so that
+// the last round is a small part of the work even when many splits are
+// empty (short caches); each split at least 64 keys, and at least 16 keys
+// per query head it serves, so the fp32 partial results written per split
+// stay within a few percent of the cache bytes it reads.
 DecodePlan decode_plan(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d) {
   DecodePlan pl;
   const int64_t R = H_q / H_kv;
   pl.head_blocks = (int)((R + 31) / 32);
   const int64_t units = B * H_kv * pl.head_blocks;
-  const int64_t target = 4096;
-  const int64_t max_splits = S_max > 0 ? (S_max + 63) / 64 : 1;
-  int64_t ns = units > 0 ? (target + units - 1) / units : 1;
-  ns = ns < 1 ? 1 : (ns > max_splits ? max_splits : ns);
-  int64_t len = S_max > 0 ? (S_max + ns - 1) / ns : kBlk;
+  const int64_t target_waves = 8 * 8 * 256;
+  const int64_t heads_per_wave = R < 32 ? R : 32;
+  int64_t len = units > 0 ? (S_max * units + target_waves - 1) / target_waves : S_max;
+  if (len < 64) len = 64;
+  if (len < 16 * heads_per_wave) len = 16 * heads_per_wave;
   len = (len + kBlk - 1) / kBlk * kBlk;
   pl.split_len = (int)len;
   pl.n_splits = (int)(S_max > 0 ? (S_max + len - 1) / len : 1);
