@@ -8,7 +8,8 @@ The 200k case also multiplies 1% of the key positions by 8 so that some
 softmax rows are sharply peaked.
 
 Seeds: 0x5A510000 + 16 * config_number + variant_index.
-Streams: q = 0, k = 1, v = 2, key-position selection = 3, cache lengths = 4.
+Streams: q = 0, k = 1, v = 2, key-position selection = 3, cache lengths = 4,
+layer input x = 6, W_qkv = 7, W_o = 8.
 
 Decode workloads (one new token per sequence against its key/value cache)
 take their head shapes from the GQA explainer's KV-cache table (32 query
@@ -27,6 +28,7 @@ from . import normal, scale_positions_bf16, select_positions, uniform
 
 SEED_BASE = 0x5A510000
 STREAM_Q, STREAM_K, STREAM_V, STREAM_SEL, STREAM_LEN = 0, 1, 2, 3, 4
+STREAM_X, STREAM_WQKV, STREAM_WO = 6, 7, 8
 
 
 @dataclass(frozen=True)
@@ -168,3 +170,56 @@ def make_decode_inputs(workload, variant_name, S_max=None, B=None):
     vv = normal(seed, STREAM_V, (B, S_max, v.H_kv, w.d), w.dtype, w.mul)
     lens = decode_lengths(w.seed(w.variants[0].name), B, S_max, w.min_len_frac)
     return q, k, vv, lens
+
+
+@dataclass(frozen=True)
+class LayerWorkload:
+    """A full attention layer (projections + attention) at one shape.  The
+    model width is the baseline's H * d; SQA variants shrink the query heads
+    (and so the q and output projections) at that width."""
+    number: int
+    name: str
+    B: int
+    S: int
+    d_model: int
+    d: int
+    causal: bool
+    variants: tuple
+    dtype: str = "bf16"
+
+    @property
+    def scale(self):
+        return 1.0 / math.sqrt(self.d)
+
+    def variant(self, name):
+        for v in self.variants:
+            if v.name == name:
+                return v
+        raise KeyError(name)
+
+    def seed(self, variant_name):
+        idx = [v.name for v in self.variants].index(variant_name)
+        return SEED_BASE + 16 * self.number + idx
+
+
+LAYER_WORKLOADS = {
+    "layer_s32k": LayerWorkload(7, "layer_s32k", B=1, S=32768, d_model=2048, d=128, causal=False,
+                                variants=(Variant("sqa", 8, 8), Variant("mha", 16, 16), Variant("xsqa", 4, 4),
+                                          Variant("gqa", 16, 4))),
+}
+
+
+def make_layer_inputs(workload, variant_name, S=None, B=None, d_model=None):
+    """x [B, S, d_model] ~ N(0, 1); W_qkv [(H_q + 2 H_kv) d, d_model] and
+    W_o [d_model, H_q d] ~ N(0, 1/fan_in) (the spread of nn.Linear's default
+    initialisation); all bf16 bits."""
+    w = workload
+    v = w.variant(variant_name)
+    S = w.S if S is None else S
+    B = w.B if B is None else B
+    dm = w.d_model if d_model is None else d_model
+    seed = w.seed(variant_name)
+    x = normal(seed, STREAM_X, (B, S, dm), w.dtype, 1.0)
+    w_qkv = normal(seed, STREAM_WQKV, ((v.H_q + 2 * v.H_kv) * w.d, dm), w.dtype, 1.0 / math.sqrt(dm))
+    w_o = normal(seed, STREAM_WO, (dm, v.H_q * w.d), w.dtype, 1.0 / math.sqrt(v.H_q * w.d))
+    return x, w_qkv, w_o

@@ -195,3 +195,46 @@ def decode(q, k, v, scale, seqlens=None, n_threads=0):
     if rc != 0:
         raise MemoryError("oracle: allocation failed")
     return out, lse_out
+
+
+def _as_f64(a):
+    """bf16 bits (uint16), float32 or float64 array -> float64 (exact)."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def layer(x, w_qkv, w_o, H_q, H_kv, d, scale, causal=False, rows=None, n_threads=0):
+    """fp64 forward of the full attention layer (GQA explainer, PyTorch module:
+    q/k/v projections, K/V shared by groups of query heads, scaled dot-product
+    attention, output projection; with the query-head count H_q free as in the
+    SQA abstract):
+
+        [q | k | v] = x W_qkv^T,   attn = attention(q, k, v),   out = attn W_o^T
+
+    x [B, S, d_model]; w_qkv [(H_q + 2 H_kv) d, d_model] (q, k, v weights stacked,
+    nn.Linear layout); w_o [d_model, H_q d].  The projections are library
+    matrix products in fp64 (no rounding in between); the attention is
+    attention() above.  rows: optional output positions (all keys are still
+    projected).  Returns float64 [B, n_rows, d_model].
+    """
+    xf, wq, wo = _as_f64(x), _as_f64(w_qkv), _as_f64(w_o)
+    B, S, dm = xf.shape
+    nq, nkv = H_q * d, H_kv * d
+    if wq.shape != (nq + 2 * nkv, dm) or wo.shape != (dm, nq):
+        raise ValueError(f"weight shapes {wq.shape} {wo.shape} do not match H_q={H_q} H_kv={H_kv} d={d} d_model={dm}")
+    kv = xf @ wq[nq:].T                                         # [B, S, 2 H_kv d]
+    k = np.ascontiguousarray(kv[..., :nkv].reshape(B, S, H_kv, d))
+    v = np.ascontiguousarray(kv[..., nkv:].reshape(B, S, H_kv, d))
+    xq = xf if rows is None else xf[:, np.asarray(rows)]
+    q_rows = xq @ wq[:nq].T                                    # [B, n, H_q d]
+    if rows is None:
+        q = np.ascontiguousarray(q_rows.reshape(B, S, H_q, d))
+        attn = attention(q, k, v, scale, causal=causal, n_threads=n_threads)
+    else:
+        # place the selected query rows at their positions; the others are unused
+        q = np.zeros((B, S, H_q, d))
+        q[:, np.asarray(rows)] = q_rows.reshape(B, -1, H_q, d)
+        attn = attention(q, k, v, scale, causal=causal, rows=rows, n_threads=n_threads)
+    return attn.reshape(B, attn.shape[1], nq) @ wo.T

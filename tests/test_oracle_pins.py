@@ -531,3 +531,68 @@ def test_decode_bf16_inputs_decode_exactly():
     b = oracle.decode(f(q), f(k), f(v), 0.17, seqlens=[50, 31])
     np.testing.assert_array_equal(a[0], b[0])
     np.testing.assert_array_equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------------------
+# full layer: projections around the attention
+
+
+def _torch_layer_module(x, w_qkv, w_o, H_q, H_kv, d, scale, causal):
+    """The GQA explainer's module structure in torch fp64 (CPU): separate q, k,
+    v linear maps, K/V expanded to the query heads with unsqueeze/expand/
+    reshape, SDPA on [B, H, T, d], output linear map."""
+    tx, tw, to = (torch.from_numpy(np.asarray(a, dtype=np.float64)) for a in (x, w_qkv, w_o))
+    B, T, _ = tx.shape
+    nq, nkv = H_q * d, H_kv * d
+    q = torch.nn.functional.linear(tx, tw[:nq]).view(B, T, H_q, d).transpose(1, 2)
+    k = torch.nn.functional.linear(tx, tw[nq:nq + nkv]).view(B, T, H_kv, d).transpose(1, 2)
+    v = torch.nn.functional.linear(tx, tw[nq + nkv:]).view(B, T, H_kv, d).transpose(1, 2)
+    R = H_q // H_kv
+    k = k.unsqueeze(2).expand(-1, -1, R, -1, -1).reshape(B, H_q, T, d)
+    v = v.unsqueeze(2).expand(-1, -1, R, -1, -1).reshape(B, H_q, T, d)
+    a = torch.nn.functional.scaled_dot_product_attention(q.contiguous(), k.contiguous(), v.contiguous(),
+                                                         is_causal=causal, scale=scale)
+    a = a.transpose(1, 2).contiguous().view(B, T, nq)
+    return torch.nn.functional.linear(a, to).numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H_q,H_kv", [(4, 4), (8, 2), (2, 2), (4, 1)])
+def test_layer_matches_torch_module_fp64(H_q, H_kv, causal):
+    rng = np.random.default_rng(300 + H_q * 10 + H_kv)
+    B, T, dm, d = 2, 19, 24, 8
+    x = rng.standard_normal((B, T, dm))
+    w_qkv = rng.standard_normal(((H_q + 2 * H_kv) * d, dm)) / math.sqrt(dm)
+    w_o = rng.standard_normal((dm, H_q * d)) / math.sqrt(H_q * d)
+    ours = oracle.layer(x, w_qkv, w_o, H_q, H_kv, d, 0.33, causal=causal)
+    ref = _torch_layer_module(x, w_qkv, w_o, H_q, H_kv, d, 0.33, causal)
+    np.testing.assert_allclose(ours, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_layer_with_selection_weights_is_plain_attention():
+    """W_qkv selecting slices of x and W_o = I reduce the layer to the
+    attention of those slices (pinned separately)."""
+    rng = np.random.default_rng(310)
+    B, T, H_q, H_kv, d = 1, 23, 4, 2, 6
+    nq, nkv = H_q * d, H_kv * d
+    dm = nq + 2 * nkv
+    x = rng.standard_normal((B, T, dm))
+    out = oracle.layer(x, np.eye(dm), np.eye(dm, nq), H_q, H_kv, d, 0.4, causal=True)
+    q = x[..., :nq].reshape(B, T, H_q, d)
+    k = x[..., nq:nq + nkv].reshape(B, T, H_kv, d)
+    v = x[..., nq + nkv:].reshape(B, T, H_kv, d)
+    att = oracle.attention(q, k, v, 0.4, causal=True).reshape(B, T, nq)
+    np.testing.assert_allclose(out, att @ np.eye(dm, nq).T, rtol=1e-13, atol=1e-14)
+
+
+def test_layer_rows_equal_full_and_bf16_decodes_exactly():
+    from inputs.configs import LAYER_WORKLOADS, make_layer_inputs
+    w = LAYER_WORKLOADS["layer_s32k"]
+    x, wq, wo = make_layer_inputs(w, "gqa", S=40, d_model=64)
+    v = w.variant("gqa")
+    full = oracle.layer(x, wq, wo, v.H_q, v.H_kv, w.d, w.scale, causal=True)
+    rows = [0, 7, 39]
+    sub = oracle.layer(x, wq, wo, v.H_q, v.H_kv, w.d, w.scale, causal=True, rows=rows)
+    np.testing.assert_allclose(sub, full[:, rows], rtol=1e-12, atol=1e-13)
+    f = lambda a: inputs.bf16_bits_to_f32(a).astype(np.float64)
+    np.testing.assert_array_equal(full, oracle.layer(f(x), f(wq), f(wo), v.H_q, v.H_kv, w.d, w.scale, causal=True))
