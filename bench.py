@@ -177,6 +177,51 @@ def time_decode(sqa, torch, wname, steps, warmup):
             "kernels": "attn_decode_split_bf16 + attn_decode_combine_bf16 (one sqa_attn_decode call)"}
 
 
+def time_layer(sqa, torch, wname, steps, warmup):
+    """Full attention layer (fused q/k/v projection GEMM, attention, output
+    projection GEMM) for every head configuration of the layer workload.
+    Credited work: 2*M*d_model*(H_q + 2 H_kv)*d + 2*M*H_q*d*d_model for the
+    projections (M = B*S tokens) plus the attention's 4*d flops per visible
+    (query, key) pair and query head."""
+    from inputs.configs import LAYER_WORKLOADS, make_layer_inputs
+    w = LAYER_WORKLOADS[wname]
+    res = {}
+    for var in w.variants:
+        x, wq, wo = make_layer_inputs(w, var.name)
+        dx, dwq, dwo = (torch.from_numpy(a).view(torch.bfloat16).to("cuda") for a in (x, wq, wo))
+        del x, wq, wo
+        out = torch.empty_like(dx)
+        ws = torch.empty(sqa.layer_workspace_size(w.B, w.S, var.H_q, var.H_kv, w.d), dtype=torch.uint8, device="cuda")
+        stream = torch.cuda.current_stream()
+
+        def run():
+            sqa.layer_fwd(dx, dwq, dwo, var.H_q, var.H_kv, out=out, scale=w.scale, causal=w.causal, stream=stream,
+                          workspace=ws)
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for i in range(steps):
+            run()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[steps]) / steps
+        M = w.B * w.S
+        proj = 2 * M * w.d_model * (var.H_q + 2 * var.H_kv) * w.d + 2 * M * var.H_q * w.d * w.d_model
+        att = algorithmic_flops(w.B, w.S, var.H_q, w.d, w.causal)
+        res[var.name] = {"H_q": var.H_q, "H_kv": var.H_kv, "ms_per_layer": round(ms, 4),
+                         "tokens_per_s": round(M / (ms * 1e-3), 1), "flops": proj + att,
+                         "tflops": round((proj + att) / (ms * 1e-3) / 1e12, 2)}
+        del dx, dwq, dwo, out, ws
+        torch.cuda.empty_cache()
+    if "mha" in res:
+        for k, r in res.items():
+            r["speedup_vs_mha"] = round(res["mha"]["ms_per_layer"] / r["ms_per_layer"], 3)
+    return {"workload": w.name, "B": w.B, "S": w.S, "d_model": w.d_model, "d": w.d, "causal": w.causal,
+            "variants": res, "kernels": "hipBLASLt GEMM + attn_fwd_bf16 + hipBLASLt GEMM (one sqa_layer_fwd call)"}
+
+
 def gemm_context(torch, n=8192, iters=10):
     """A plain bf16 GEMM from the vendor library on random N(0,1) data, as a
     practical reference for dense bf16 throughput on this GPU (the chip is
@@ -245,6 +290,9 @@ def main():
     ap.add_argument("--decode", choices=["auto", "none", "only"], default="auto",
                     help="time the decode workload too (auto), or only it")
     ap.add_argument("--decode-workload", default="decode_s128k")
+    ap.add_argument("--layer", choices=["auto", "none", "only"], default="auto",
+                    help="time the full attention layer too (auto), or only it")
+    ap.add_argument("--layer-workload", default="layer_s32k")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -274,6 +322,10 @@ def main():
 
     w = WORKLOADS[args.workload]
     sqa.load_library()
+    if args.layer == "only":
+        print(json.dumps({"layer": time_layer(sqa, torch, args.layer_workload, args.steps, args.warmup)}),
+              flush=True)
+        return
     if args.decode == "only":
         print(json.dumps({"decode": time_decode(sqa, torch, args.decode_workload, args.steps, args.warmup)}),
               flush=True)
@@ -300,6 +352,7 @@ def main():
     bwd = (time_backward(sqa, torch, w, args.variant, max(3, args.steps // 2), args.warmup)
            if args.backward == "auto" and w.dtype == "bf16" else None)
     dec = time_decode(sqa, torch, args.decode_workload, 20, 3) if args.decode == "auto" else None
+    lay = time_layer(sqa, torch, args.layer_workload, 5, 2) if args.layer == "auto" else None
     cpu = cpu_baseline(w, args.variant, args.cpu_budget) if args.cpu_budget > 0 else None
     gemm = gemm_context(torch) if args.cpu_budget > 0 else None
     v = w.variant(args.variant)
@@ -328,6 +381,7 @@ def main():
         "roofline": roofline,
         "backward": bwd,
         "decode": dec,
+        "layer": lay,
         "cpu_baseline": cpu,
         "pages_claim": "SQA abstract: up to 3x throughput on 32k-200k sequences; hardware not named",
         "context_library_gemm": gemm,

@@ -185,6 +185,45 @@ sqa_status sqa_attn_decode(const void* q, const void* k_cache, const void* v_cac
 /* Workspace bytes sqa_attn_decode needs; -1 for invalid sizes. */
 int64_t sqa_attn_decode_workspace_size(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d);
 
+/*
+ * Full attention layer forward with decoupled head counts: the GQA
+ * explainer's PyTorch module (q/k/v projections, K/V heads shared by groups
+ * of query heads, scaled dot-product attention, output projection; section on
+ * the PyTorch implementation) with the query-head count free, as Sparse Query
+ * Attention proposes (SQA abstract: fewer query heads, so fewer attention
+ * FLOPs and narrower q and output projections):
+ *
+ *   [q | k | v] = x W_qkv^T,   attn = sqa_attn_fwd(q, k, v),   out = attn W_o^T
+ *
+ *   x          [B, S, d_model] bf16, device, 16-byte aligned
+ *   w_qkv      [(H_q + 2 H_kv) d, d_model] bf16: the q, k and v projection
+ *              weights (nn.Linear layout, out x in) stacked in that order;
+ *              rows h d ... h d + d - 1 of each block belong to head h
+ *   w_o        [d_model, H_q d] bf16 (nn.Linear layout)
+ *   out        [B, S, d_model] bf16 output
+ *   workspace  caller-owned device scratch of at least
+ *              sqa_layer_workspace_size(B, S, H_q, H_kv, d) bytes, 16-byte
+ *              aligned: the projection output, the attention output and the
+ *              GEMM library's workspace; overwritten
+ *   B, S, H_q, H_kv, d, scale, causal, stream   as for sqa_attn_fwd
+ *
+ * The projections run on hipBLASLt (bf16 inputs and outputs, fp32
+ * accumulation); the library creates one hipBLASLt handle per device on
+ * first use and keeps it, with the chosen GEMM algorithms, until the process
+ * ends.  q, k and v are rounded to bf16 after the projection and the
+ * attention output before the output projection.  out must not overlap any
+ * input or the workspace; the workspace must not overlap any input.
+ * SQA_ERR_INVALID_ARGUMENT as for sqa_attn_fwd (also d_model < 1 or a short
+ * workspace); SQA_ERR_UNSUPPORTED for d not in {32, 64, 128}, d_model not a
+ * multiple of 8 or S > 2^30; SQA_ERR_HIP for a HIP or hipBLASLt failure.
+ */
+sqa_status sqa_layer_fwd(const void* x, const void* w_qkv, const void* w_o, void* out, void* workspace,
+                         int64_t workspace_bytes, int64_t B, int64_t S, int32_t d_model, int32_t H_q, int32_t H_kv,
+                         int32_t d, float scale, int causal, sqa_stream_t stream);
+
+/* Workspace bytes sqa_layer_fwd needs; -1 for invalid sizes. */
+int64_t sqa_layer_workspace_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv, int32_t d);
+
 /* Static, NUL-terminated description of a status code. */
 const char* sqa_status_string(sqa_status status);
 

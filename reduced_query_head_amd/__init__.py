@@ -1,5 +1,5 @@
 """Python binding of libsqa: decoupled-head attention on MI355X (forward,
-backward, decode).
+backward, decode, full layer).
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``lib/libsqa.so`` (sources in ``csrc/``, C-ABI in
@@ -50,6 +50,11 @@ def load_library(path=None):
                                     ctypes.c_float, vp]
     lib.sqa_attn_decode_workspace_size.restype = i64
     lib.sqa_attn_decode_workspace_size.argtypes = [i64, i64, i32, i32, i32]
+    lib.sqa_layer_fwd.restype = ctypes.c_int
+    lib.sqa_layer_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, ctypes.c_float, ctypes.c_int,
+                                  vp]
+    lib.sqa_layer_workspace_size.restype = i64
+    lib.sqa_layer_workspace_size.argtypes = [i64, i64, i32, i32, i32]
     lib.sqa_status_string.restype = ctypes.c_char_p
     lib.sqa_status_string.argtypes = [ctypes.c_int]
     _lib = lib
@@ -241,3 +246,57 @@ def attn_decode(q, k_cache, v_cache, seqlens=None, out=None, scale=None, stream=
     if st != SQA_OK:
         raise SqaError(st, status_string(st))
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def layer_workspace_size(B, S, H_q, H_kv, d):
+    return int(load_library().sqa_layer_workspace_size(B, S, H_q, H_kv, d))
+
+
+def layer_fwd_raw(x, w_qkv, w_o, out, workspace, workspace_bytes, B, S, d_model, H_q, H_kv, d, scale, causal, stream):
+    """Direct call of sqa_layer_fwd with integer device addresses; returns the status."""
+    return load_library().sqa_layer_fwd(x, w_qkv, w_o, out, workspace, workspace_bytes, B, S, d_model, H_q, H_kv, d,
+                                        scale, int(causal), stream)
+
+
+def layer_fwd(x, w_qkv, w_o, H_q, H_kv, out=None, scale=None, causal=False, stream=None, workspace=None):
+    """Attention layer forward: [q|k|v] = x W_qkv^T, attention with H_q query
+    and H_kv K/V heads (head size (W_qkv rows) / (H_q + 2 H_kv)), out = attn W_o^T.
+
+    x: [B, S, d_model]; w_qkv: [(H_q + 2 H_kv) d, d_model]; w_o: [d_model, H_q d];
+    contiguous bfloat16 GPU tensors.  A uint8 workspace of
+    layer_workspace_size(B, S, H_q, H_kv, d) bytes is allocated if none is given.
+    """
+    import torch
+
+    for name, t in (("x", x), ("w_qkv", w_qkv), ("w_o", w_o)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bfloat16 GPU tensor")
+    if x.dim() != 3 or w_qkv.dim() != 2 or w_o.dim() != 2:
+        raise ValueError("expected x [B,S,d_model], w_qkv [(H_q+2H_kv)d, d_model], w_o [d_model, H_q d]")
+    B, S, d_model = x.shape
+    rows_qkv = w_qkv.shape[0]
+    if rows_qkv % (H_q + 2 * H_kv) != 0:
+        raise ValueError("w_qkv rows must be (H_q + 2 H_kv) * d")
+    d = rows_qkv // (H_q + 2 * H_kv)
+    if w_qkv.shape[1] != d_model or tuple(w_o.shape) != (d_model, H_q * d):
+        raise ValueError(f"weight shapes {tuple(w_qkv.shape)} {tuple(w_o.shape)} do not match x {tuple(x.shape)}")
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous GPU tensor shaped and typed like x")
+    ws_bytes = layer_workspace_size(B, S, H_q, H_kv, d)
+    if ws_bytes < 0:
+        raise ValueError("invalid sizes")
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = layer_fwd_raw(x.data_ptr(), w_qkv.data_ptr(), w_o.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+                       workspace.numel() * workspace.element_size(), B, S, d_model, H_q, H_kv, d, float(scale),
+                       causal, handle)
+    if st != SQA_OK:
+        raise SqaError(st, status_string(st))
+    return out

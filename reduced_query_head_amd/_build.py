@@ -5,13 +5,15 @@ import subprocess
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["csrc/api.cpp", "csrc/attn_fwd.hip", "csrc/attn_bwd.hip", "csrc/attn_decode.hip"]
+SOURCES = ["csrc/api.cpp", "csrc/attn_fwd.hip", "csrc/attn_bwd.hip", "csrc/attn_decode.hip", "csrc/layer.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
     # no packed-fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
 ]
+# the layer's projections call hipBLASLt
+LIBS = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
 
 
 def lib_path():
@@ -22,7 +24,7 @@ def build(verbose=False):
     out = lib_path()
     os.makedirs(os.path.dirname(out), exist_ok=True)
     tmp = out + ".tmp"
-    cmd = [HIPCC] + FLAGS + [os.path.join(_HERE, s) for s in SOURCES] + ["-o", tmp]
+    cmd = [HIPCC] + FLAGS + [os.path.join(_HERE, s) for s in SOURCES] + LIBS + ["-o", tmp]
     if verbose:
         print(" ".join(cmd))
     res = subprocess.run(cmd, capture_output=True, text=True)

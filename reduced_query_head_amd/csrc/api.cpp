@@ -96,6 +96,8 @@ SQA_API sqa_status sqa_attn_fwd_lse(const void* q, const void* k, const void* v,
   a.negate_q = scale < 0.f;
   a.causal = causal;
   a.stream = (void*)stream;
+  a.q_stride = (int64_t)H_q * d;
+  a.kv_stride = (int64_t)H_kv * d;
   return sqa::launch_attn_fwd(a) == hipSuccess ? SQA_OK : SQA_ERR_HIP;
 }
 
@@ -241,4 +243,65 @@ SQA_API sqa_status sqa_attn_decode(const void* q, const void* k_cache, const voi
   a.negate_q = scale < 0.f;
   a.stream = (void*)stream;
   return sqa::launch_attn_decode(a) == hipSuccess ? SQA_OK : SQA_ERR_HIP;
+}
+
+SQA_API int64_t sqa_layer_workspace_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv, int32_t d) {
+  if (B < 0 || S < 0 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || d < 1) return -1;
+  int64_t rows, t;
+  if (!mul_ok(B, S, &rows) || !mul_ok(rows, (int64_t)(H_q + 2 * H_kv) * d * 4, &t)) return -1;
+  return sqa::layer_plan(B, S, H_q, H_kv, d).workspace_bytes;
+}
+
+SQA_API sqa_status sqa_layer_fwd(const void* x, const void* w_qkv, const void* w_o, void* out, void* workspace,
+                                 int64_t workspace_bytes, int64_t B, int64_t S, int32_t d_model, int32_t H_q,
+                                 int32_t H_kv, int32_t d, float scale, int causal, sqa_stream_t stream) {
+  if (B < 0 || S < 0 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || d < 1 || d_model < 1)
+    return SQA_ERR_INVALID_ARGUMENT;
+  if (causal != 0 && causal != 1) return SQA_ERR_INVALID_ARGUMENT;
+  if (!isfinite(scale)) return SQA_ERR_INVALID_ARGUMENT;
+  if (B == 0 || S == 0) return SQA_OK;
+  if (!x || !w_qkv || !w_o || !out || !workspace) return SQA_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)x | (uintptr_t)w_qkv | (uintptr_t)w_o | (uintptr_t)out | (uintptr_t)workspace) & 15u)
+    return SQA_ERR_INVALID_ARGUMENT;
+  int64_t rows, x_bytes, wqkv_bytes, wo_bytes, ws_probe;
+  const int64_t n_qkv = (int64_t)(H_q + 2 * H_kv) * d;
+  if (!mul_ok(B, S, &rows) || !mul_ok(rows, (int64_t)d_model * 2, &x_bytes) ||
+      !mul_ok(n_qkv, (int64_t)d_model * 2, &wqkv_bytes) || !mul_ok((int64_t)H_q * d, (int64_t)d_model * 2, &wo_bytes) ||
+      !mul_ok(rows, n_qkv * 4, &ws_probe))   // the workspace sizes stay representable
+    return SQA_ERR_INVALID_ARGUMENT;
+  const sqa::LayerPlan lp = sqa::layer_plan(B, S, H_q, H_kv, d);
+  if (workspace_bytes < lp.workspace_bytes) return SQA_ERR_INVALID_ARGUMENT;
+  const void* ins[3] = {x, w_qkv, w_o};
+  const int64_t in_bytes[3] = {x_bytes, wqkv_bytes, wo_bytes};
+  for (int j = 0; j < 3; ++j)
+    if (ranges_overlap(out, x_bytes, ins[j], in_bytes[j]) ||
+        ranges_overlap(workspace, lp.workspace_bytes, ins[j], in_bytes[j]))
+      return SQA_ERR_INVALID_ARGUMENT;
+  if (ranges_overlap(out, x_bytes, workspace, lp.workspace_bytes)) return SQA_ERR_INVALID_ARGUMENT;
+  if (d != 32 && d != 64 && d != 128) return SQA_ERR_UNSUPPORTED;
+  // rows of x, W_qkv and W_o must stay 16-byte aligned for the GEMM library
+  if (d_model % 8 != 0) return SQA_ERR_UNSUPPORTED;
+  if (S > (int64_t)1 << 30 || sqa::bf16_grid_size(B, S, H_q, H_kv) > INT32_MAX) return SQA_ERR_UNSUPPORTED;
+
+  sqa::LayerArgs a;
+  a.x = x;
+  a.w_qkv = w_qkv;
+  a.w_o = w_o;
+  a.out = out;
+  a.workspace = workspace;
+  a.B = B;
+  a.S = S;
+  a.d_model = d_model;
+  a.H_q = H_q;
+  a.H_kv = H_kv;
+  a.d = d;
+  const float log2e = 1.4426950408889634f;
+  const float mag = fabsf(scale);
+  a.c = mag > 0.f ? mag * log2e : 1e-30f;
+  if (!isfinite(a.c)) return SQA_ERR_INVALID_ARGUMENT;
+  a.negate_q = scale < 0.f;
+  a.causal = causal;
+  a.stream = (void*)stream;
+  bool lib_error = false;
+  return sqa::launch_layer_fwd(a, &lib_error) == hipSuccess ? SQA_OK : SQA_ERR_HIP;
 }

@@ -67,6 +67,8 @@ struct Bf16Params {
   float c;               // |scale| * log2(e), strictly positive
   uint32_t q_sign;       // 0x8000 when scale < 0: q is negated on load (exact)
   float* lse;            // optional [B, S, H_q] row log-normaliser (natural log)
+  int64_t q_stride;      // elements between consecutive positions of q (H_q * D when dense)
+  int64_t kv_stride;     // same for k and v (H_kv * D when dense)
 };
 
 template <int D, bool CAUSAL, int WAVES, int KEYS>
@@ -105,9 +107,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_bf16(Bf16Params p) {
   const int wg_last_pos = min((last_item / p.R) * kRows + kRows - 1, S - 1);
   const int n_tiles = CAUSAL ? wg_last_pos / KEYS + 1 : (S + KEYS - 1) / KEYS;
 
-  const int64_t kv_stride = (int64_t)p.H_kv * D;
-  const uint16_t* k_base = p.k + ((int64_t)b * S * p.H_kv + g) * D;
-  const uint16_t* v_base = p.v + ((int64_t)b * S * p.H_kv + g) * D;
+  const int64_t kv_stride = p.kv_stride;
+  const uint16_t* k_base = p.k + (int64_t)b * S * kv_stride + g * D;
+  const uint16_t* v_base = p.v + (int64_t)b * S * kv_stride + g * D;
 
   TileCopy<D, WAVES, KEYS> cp;
   cp.init(kv_stride, wave, lane);
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_bf16(Bf16Params p) {
   bf16x8 qf[KS];
   {
     const int qrow = min(pos0 + col, S - 1);
-    const uint16_t* qp = p.q + (((int64_t)b * S + qrow) * p.H_q + h) * D + half * 8;
+    const uint16_t* qp = p.q + ((int64_t)b * S + qrow) * p.q_stride + h * D + half * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 raw = *(const u32x4*)(qp + ks * 16);
@@ -350,6 +352,8 @@ hipError_t launch_bf16_w(const LaunchArgs& a) {
   p.c = a.c;
   p.q_sign = a.negate_q ? 0x8000u : 0u;
   p.lse = a.lse;
+  p.q_stride = a.q_stride;
+  p.kv_stride = a.kv_stride;
   const int64_t grid = (int64_t)p.n_groups * p.chunks;
   hipLaunchKernelGGL((attn_fwd_bf16<D, CAUSAL, WAVES, KEYS>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
                      (hipStream_t)a.stream, p);

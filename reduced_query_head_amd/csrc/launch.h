@@ -23,6 +23,8 @@ struct LaunchArgs {
   bool negate_q;   // scale < 0
   int causal;
   void* stream;
+  int64_t q_stride;   // elements between consecutive positions of q (bf16 path; H_q * d when dense)
+  int64_t kv_stride;  // same for k and v (bf16 path; H_kv * d when dense)
 };
 
 hipError_t launch_attn_fwd(const LaunchArgs& a);
@@ -85,6 +87,36 @@ struct DecodePlan {
 
 DecodePlan decode_plan(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d);
 hipError_t launch_attn_decode(const DecodeArgs& a);
+
+struct LayerArgs {
+  const void* x;        // [B, S, d_model] bf16
+  const void* w_qkv;    // [(H_q + 2 H_kv) d, d_model] bf16
+  const void* w_o;      // [d_model, H_q d] bf16
+  void* out;            // [B, S, d_model] bf16
+  void* workspace;      // layer_plan(...).workspace_bytes bytes
+  int64_t B;
+  int64_t S;
+  int32_t d_model;
+  int32_t H_q;
+  int32_t H_kv;
+  int32_t d;
+  float c;              // |scale| * log2(e), or a tiny positive value when scale == 0
+  bool negate_q;        // scale < 0
+  int causal;
+  void* stream;
+};
+
+struct LayerPlan {
+  int64_t n_qkv;            // (H_q + 2 H_kv) d, the fused projection width
+  int64_t qkv_bytes;        // projection output, 256-byte rounded
+  int64_t attn_bytes;       // attention output, 256-byte rounded
+  int64_t gemm_ws_bytes;    // workspace offered to the GEMM library
+  int64_t workspace_bytes;
+};
+
+LayerPlan layer_plan(int64_t B, int64_t S, int32_t H_q, int32_t H_kv, int32_t d);
+// lib_error is set when the GEMM library (not the HIP runtime) failed
+hipError_t launch_layer_fwd(const LayerArgs& a, bool* lib_error);
 
 }  // namespace sqa
 

@@ -173,3 +173,38 @@ def test_decode_empty_and_optional_pointers():
     assert _call_dec(B=0, q=0, k=0, v=0, out=0, ws=0) == sqa.SQA_OK
     # seqlens and lse are optional; they still may not be misaligned (checked above)
     assert _call_dec(B=0, seqlens=0, lse=0) == sqa.SQA_OK
+
+
+def _call_layer(**kw):
+    a = dict(x=FAKE, wqkv=FAKE + G, wo=FAKE + 2 * G, out=FAKE + 3 * G, ws=FAKE + 4 * G, ws_bytes=None, B=1, S=1024,
+             d_model=2048, H_q=8, H_kv=8, d=128, scale=0.088, causal=0)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = max(0, sqa.layer_workspace_size(a["B"], a["S"], a["H_q"], a["H_kv"], a["d"]))
+    return sqa.layer_fwd_raw(a["x"], a["wqkv"], a["wo"], a["out"], a["ws"], a["ws_bytes"], a["B"], a["S"],
+                             a["d_model"], a["H_q"], a["H_kv"], a["d"], a["scale"], a["causal"], 0)
+
+
+def test_layer_workspace_size():
+    n = sqa.layer_workspace_size(1, 1024, 8, 8, 128)
+    # the projection output and the attention output at least
+    assert n >= 1024 * (8 + 16) * 128 * 2 + 1024 * 8 * 128 * 2
+    assert sqa.layer_workspace_size(1, 10, 6, 4, 64) == -1 and sqa.layer_workspace_size(-1, 10, 4, 4, 64) == -1
+
+
+@pytest.mark.parametrize("kw", [
+    dict(H_q=6, H_kv=4), dict(d_model=0), dict(B=-1), dict(causal=3), dict(scale=float("nan")),
+    dict(x=0), dict(wqkv=0), dict(wo=0), dict(out=0), dict(ws=0), dict(x=FAKE + 4), dict(ws=FAKE + 4 * G + 8),
+    dict(ws_bytes=1024), dict(out=FAKE + 4096), dict(ws=FAKE + G + 256), dict(out=FAKE + 4 * G + 512),
+])
+def test_layer_invalid(kw):
+    assert _call_layer(**kw) == sqa.SQA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [dict(d=96), dict(d=16), dict(d_model=2044)])
+def test_layer_unsupported(kw):
+    assert _call_layer(**kw) == sqa.SQA_ERR_UNSUPPORTED
+
+
+def test_layer_empty():
+    assert _call_layer(S=0, x=0, wqkv=0, wo=0, out=0, ws=0) == sqa.SQA_OK
