@@ -17,11 +17,15 @@
 //    along MFMA M (S^T = K Q^T, dP^T = V dO^T) each lane owns one query, so
 //    D_i and lse_i are per-lane scalars; dQ^T += K^T dS^T reads K^T with
 //    transposing LDS reads.
-//  * bwd_dkdv: one wave per 32 keys of one K/V head, K and V held in
-//    registers; query tiles of 64 rows (Q, dO and their statistics) of all R
-//    query heads of the group stream through LDS.  S = Q K^T and dP = dO V^T
-//    put keys on lanes, so dV^T += dO^T P and dK^T += Q^T dS take P and dS
-//    straight from the accumulators and dO^T, Q^T from transposing LDS reads.
+//  * bwd_dkdv: one wave per 32 keys of one K/V head (one wave per SIMD),
+//    its K and V rows staged once in LDS; query tiles of 64 rows (Q, dO and
+//    their statistics) of all R query heads of the group stream through LDS.
+//    S = Q K^T and dP = dO V^T put keys on lanes, so dV^T += dO^T P and
+//    dK^T += Q^T dS take P and dS straight from the accumulators and dO^T,
+//    Q^T from transposing LDS reads.  The two 32-query halves of a tile form
+//    a two-stage pipeline in the instruction stream (half 1's products
+//    between half 0's softmax instructions and so on), since no second wave
+//    on the SIMD can fill the gaps.
 //
 // All matrix products are bf16 MFMA with fp32 accumulation; P and dS are
 // rounded to bf16 for the products that consume them.  The fp32 path is plain
@@ -70,7 +74,8 @@ struct BwdParams {
 };
 
 // ---------------------------------------------------------------------------
-// stats: delta and lse2 rows, transposed to [B, H_q, S_pad]; pad entries 0.
+// stats: delta and lse2 rows, transposed to [B, H_q, S_pad]; pad entries:
+// delta 0, lse2 +inf.
 // 8 lanes per (b, i, h) row.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_stats_bf16(BwdParams p, int64_t B) {
@@ -103,7 +108,9 @@ __global__ __launch_bounds__(256) void bwd_stats_bf16(BwdParams p, int64_t B) {
   if (row < total && sub == 0) {
     const bool valid = i < p.S;
     p.ws_delta[row] = valid ? acc : 0.f;
-    p.ws_lse2[row] = valid ? p.lse[(b * p.S + i) * p.H_q + h] * 1.4426950408889634f : 0.f;
+    // pad rows get lse2 = +inf, so their probabilities 2^(c s - lse2) are
+    // exactly 0 wherever they are recomputed (no per-element tail mask)
+    p.ws_lse2[row] = valid ? p.lse[(b * p.S + i) * p.H_q + h] * 1.4426950408889634f : __builtin_inff();
   }
 }
 
@@ -269,6 +276,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds_g1[TILE];
   __shared__ __attribute__((aligned(1024))) float lds_s0[256];  // [0,64) lse2, [64,128) delta
   __shared__ __attribute__((aligned(1024))) float lds_s1[256];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_kk[KEYS_WG * D];   // this workgroup's K rows
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_vv[KEYS_WG * D];   // and V rows
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -313,19 +322,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
   // K^T and V^T as B operands: lane holds key my_key, dims ks*16 + half*8 ...
   // A negative scale is folded into k here (q streams through LDS unchanged),
   // so that c * s = scale * log2(e) * <q, k> with c = |scale| * log2(e).
-  bf16x8 kf[KS], vf[KS];
+  // K and V rows of this wave's keys go to LDS once (the K sign flipped for
+  // a negative scale); the products read them back as B operands: lane holds
+  // key my_key, dims ks*16 + half*8 ...
   {
     const int krow = min(my_key, S - 1);
     const int64_t off = (((int64_t)b * S + krow) * p.H_kv + g) * D + half * 8;
     const uint32_t sgn = p.q_sign * 0x10001u;
+    const int row = wave * kRows32 + col;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 raw = *(const u32x4*)(p.k + off + ks * 16);
       raw ^= (u32x4){sgn, sgn, sgn, sgn};
-      kf[ks] = __builtin_bit_cast(bf16x8, raw);
-      vf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(p.v + off + ks * 16));
+      *(SQA_LDS u32x4*)((SQA_LDS uint16_t*)lds_kk + tile_off<D>(row, ks * 16 + half * 8)) = raw;
+      *(SQA_LDS u32x4*)((SQA_LDS uint16_t*)lds_vv + tile_off<D>(row, ks * 16 + half * 8)) =
+          *(const u32x4*)(p.v + off + ks * 16);
     }
   }
+  int b_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) b_off[ks] = tile_off<D>(wave * kRows32 + col, ks * 16 + half * 8);
   if (U > 0) issue_tile(0, (SQA_LDS uint16_t*)lds_q0, (SQA_LDS uint16_t*)lds_g0, (SQA_LDS float*)lds_s0);
 
   int a_off[KS];  // Q / dO rows as the A operand: row col of the 32-row half
@@ -352,45 +368,71 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
     if (u + 1 < U) issue_tile(u + 1, qn, gn, sn);
     const int qt = qt_first + u % qt_count;
     const int q0 = qt * QT;
-    if (CAUSAL && q0 + QT - 1 < key0) return;  // whole tile before this wave's keys
-#pragma unroll
-    for (int qh = 0; qh < QT / 32; ++qh) {
-      const int qbase = q0 + qh * 32;
-      if (CAUSAL && qbase + 31 < key0) continue;
-      // S = Q K^T and dP = dO V^T (queries along M, this lane's key along N)
-      f32x16 s = (f32x16){}, dp = (f32x16){};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *(const SQA_LDS bf16x8*)(qt_l + qh * 32 * D + a_off[ks]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], s, 0, 0, 0);
-        const bf16x8 ga = *(const SQA_LDS bf16x8*)(gt_l + qh * 32 * D + a_off[ks]);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
-      }
-      lds_mfma_pipeline_hint<2 * KS, 1, 4>();
-      // query of register r: qbase + 8*(r/4) + 4*half + r%4
-      float l2[16], dl[16];
+    if (CAUSAL ? q0 + QT - 1 < key0 : q0 >= S) return;  // tile before this wave's keys / past the end
+    // Both 32-query halves of the tile, as a two-stage pipeline: the S/dP
+    // products of half 1 issue between the softmax instructions of half 0, and
+    // the dV/dK products of half 0 between those of half 1 (one wave per SIMD
+    // here, so the overlap has to come from this wave's own instruction order).
+    constexpr int NH = QT / 32;
+    // row statistics of one half (lse2, delta), read just before its softmax
+    auto load_stats = [&](int qh, float (&l2)[16], float (&dl)[16]) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x4 a = *(const SQA_LDS f32x4*)(st_l + qh * 32 + 8 * j + 4 * half);
         const f32x4 d4 = *(const SQA_LDS f32x4*)(st_l + 64 + qh * 32 + 8 * j + 4 * half);
-        l2[4 * j] = a[0]; l2[4 * j + 1] = a[1]; l2[4 * j + 2] = a[2]; l2[4 * j + 3] = a[3];
-        dl[4 * j] = d4[0]; dl[4 * j + 1] = d4[1]; dl[4 * j + 2] = d4[2]; dl[4 * j + 3] = d4[3];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          l2[4 * j + e] = a[e];
+          dl[4 * j + e] = d4[e];
+        }
       }
-      const bool need_mask = (qbase + 32 > S) || (CAUSAL && qbase < key0 + 31);
+    };
+    float l2a[16], dla[16];
+    load_stats(0, l2a, dla);
+    // S = Q K^T and dP = dO V^T (queries along M, this lane's key along N)
+    f32x16 s[NH], dp[NH];
+#pragma unroll
+    for (int qh = 0; qh < NH; ++qh) {
+      s[qh] = (f32x16){};
+      dp[qh] = (f32x16){};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = *(const SQA_LDS bf16x8*)(qt_l + qh * 32 * D + a_off[ks]);
+        const bf16x8 kb = *(const SQA_LDS bf16x8*)((const SQA_LDS uint16_t*)lds_kk + b_off[ks]);
+        s[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kb, s[qh], 0, 0, 0);
+        const bf16x8 ga = *(const SQA_LDS bf16x8*)(gt_l + qh * 32 * D + a_off[ks]);
+        const bf16x8 vb = *(const SQA_LDS bf16x8*)((const SQA_LDS uint16_t*)lds_vv + b_off[ks]);
+        dp[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vb, dp[qh], 0, 0, 0);
+      }
+    }
+    // P and dS = P (dP - D), rounded to bf16; query of register r:
+    // qbase + 8*(r/4) + 4*half + r%4
+    bf16x8 pk[NH][2], dsk[NH][2];
+#pragma unroll
+    for (int qh = 0; qh < NH; ++qh) {
+      float l2b[16], dlb[16];
+      if (qh == 1) load_stats(1, l2b, dlb);
+      const float* l2 = qh == 0 ? l2a : l2b;
+      const float* dl = qh == 0 ? dla : dlb;
+      const int qbase = q0 + qh * 32;
+      // rows past S have lse2 = +inf (P = 0); only the causal mask is explicit
+      const bool need_mask = CAUSAL && qbase < key0 + 31;
       const int qlo = qbase + 4 * half;
-      bf16x8 pk[2], dsk[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = st * 8 + e;
           const int qi = qlo + 8 * (r >> 2) + (r & 3);
-          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2[r]));
-          if (need_mask && ((qi >= S) || (CAUSAL && my_key > qi))) pv = 0.f;
-          pk[st][e] = (__bf16)pv;
-          dsk[st][e] = (__bf16)(pv * (dp[r] - dl[r]));
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qh][r], c, -l2[r]));
+          if (need_mask && my_key > qi) pv = 0.f;
+          pk[qh][st][e] = (__bf16)pv;
+          dsk[qh][st][e] = (__bf16)(pv * (dp[qh][r] - dl[r]));
         }
-      // dV^T += dO^T P and dK^T += Q^T dS (16 queries per MFMA step)
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS (16 queries per MFMA step)
+#pragma unroll
+    for (int qh = 0; qh < NH; ++qh)
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -399,13 +441,38 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
           const bf16x4 glo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SQA_LDS bf16x4*)(gt_l + ro + t_off[db][0]));
           const bf16x4 ghi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SQA_LDS bf16x4*)(gt_l + ro + t_off[db][1]));
           dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                           pk[st], dv[db], 0, 0, 0);
+                                                           pk[qh][st], dv[db], 0, 0, 0);
           const bf16x4 qlo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SQA_LDS bf16x4*)(qt_l + ro + t_off[db][0]));
           const bf16x4 qhi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SQA_LDS bf16x4*)(qt_l + ro + t_off[db][1]));
           dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(qlo4, qhi4, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                           dsk[st], dk[db], 0, 0, 0);
+                                                           dsk[qh][st], dk[db], 0, 0, 0);
         }
-      lds_mfma_pipeline_hint<4 * DB, 2, 4>();
+    // instruction order: half-0 stats and S/dP reads; half-0 S/dP; half-1 S/dP
+    // with half-0 softmax; half-0 dV/dK with half-1 softmax; half-1 dV/dK
+    static_assert(NH == 2, "the schedule below is written for two query halves");
+    __builtin_amdgcn_sched_group_barrier(0x100, 8 + 8, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4 * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4 * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
   for (int u = 0; u < U; u += 2) {
