@@ -287,6 +287,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0 = skip)")
     ap.add_argument("--backward", choices=["auto", "none", "only"], default="auto",
                     help="time the backward too (auto: bf16 workloads), or only it")
+    ap.add_argument("--long", choices=["auto", "none"], default="auto",
+                    help="also time the 131k causal and 200k ragged workloads (SQA and comparators)")
     ap.add_argument("--decode", choices=["auto", "none", "only"], default="auto",
                     help="time the decode workload too (auto), or only it")
     ap.add_argument("--decode-workload", default="decode_s128k")
@@ -349,6 +351,19 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": traffic_from_profile(w.name, args.variant),
                 "kernel": f"attn_fwd_bf16<d={w.d},causal={int(w.causal)}>",
                 "flops_per_launch": main_res["flops"], "avg_launch_ms": round(main_res["avg_launch_ms"], 4)}
+    longctx = None
+    if args.long == "auto" and args.workload == "encoder_s32k":
+        longctx = {}
+        for wn in ("causal_s131k", "ragged_s200k"):
+            lw = WORKLOADS[wn]
+            rs = {vv.name: time_variant(sqa, torch, lw, vv.name, 5, 2) for vv in lw.variants}
+            first = lw.variants[0].name
+            longctx[wn] = {k: {"H_q": r["H_q"], "H_kv": r["H_kv"], "ms_per_step": round(r["ms_per_step"], 3),
+                               "tflops": round(r["tflops"], 1),
+                               "pct_peak": round(100 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
+                               "tokens_per_s": round(r["tokens_per_s"], 1),
+                               "sqa_speedup": round(r["ms_per_step"] / rs[first]["ms_per_step"], 3) if k != first else 1.0}
+                           for k, r in rs.items()}
     bwd = (time_backward(sqa, torch, w, args.variant, max(3, args.steps // 2), args.warmup)
            if args.backward == "auto" and w.dtype == "bf16" else None)
     dec = time_decode(sqa, torch, args.decode_workload, 20, 3) if args.decode == "auto" else None
@@ -379,6 +394,7 @@ def main():
                             "sqa_speedup": round(c["sqa_speedup"], 3), "ideal_speedup": c["ideal_speedup"]}
                         for k, c in comps.items()},
         "roofline": roofline,
+        "long_context": longctx,
         "backward": bwd,
         "decode": dec,
         "layer": lay,
