@@ -80,6 +80,9 @@ CASES = [
     (4, 2048, 16, 4, 128, [2048, 5000, 31, 1500]),   # a length above S_max counts as S_max
     (1, 9000, 8, 8, 128, None),               # no length array: S_max everywhere
     (3, 33000, 32, 8, 128, [33000, 20001, 65]),
+    # many short sequences: seeded lengths in [0, 600] with 0, 1 and over-long entries
+    (64, 512, 32, 8, 128, [0, 1, 600] + [int(x) for x in np.random.default_rng(64).integers(0, 601, 61)]),
+    (2, 1000, 128, 1, 64, [1000, 517]),      # 128 heads per group: four head blocks
 ]
 
 

@@ -38,7 +38,8 @@ SMALL = [
     (1, 129, 16, 1, 128, True), (1, 257, 6, 2, 128, False), (3, 200, 6, 3, 64, True),
     (1, 1000, 8, 8, 128, True), (1, 1000, 8, 2, 128, False), (2, 513, 16, 4, 64, False),
     (1, 777, 4, 1, 32, True), (2, 96, 2, 2, 32, False), (1, 2048, 16, 16, 128, True),
-    (1, 1500, 12, 4, 128, True), (1, 300, 32, 2, 64, True),
+    (1, 1500, 12, 4, 128, True), (1, 300, 32, 2, 64, True), (4, 333, 8, 1, 128, True),
+    (1, 3000, 128, 4, 64, False),
     # grids large enough for the 8-wave, 128-key-tile kernel (ragged tails)
     (2, 1100, 64, 8, 128, True), (1, 1800, 64, 64, 64, False), (1, 4100, 32, 2, 128, True),
 ]
