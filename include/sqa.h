@@ -157,13 +157,13 @@ int64_t sqa_attn_bwd_workspace_size(int64_t B, int64_t S, int32_t H_q);
  * with g = floor(h / (H_q/H_kv)) as in sqa_attn_fwd: the causal forward's
  * row len_b - 1, for a token whose own key/value is already in the cache.
  *
- *   q          [B, H_q, d] bf16, device, 16-byte aligned
- *   k_cache    [B, S_max, H_kv, d] bf16 (BSHD), device, 16-byte aligned;
+ *   q          [B, H_q, d] of `dtype`, device, 16-byte aligned
+ *   k_cache    [B, S_max, H_kv, d] of `dtype` (BSHD), device, 16-byte aligned;
  *   v_cache    positions >= len_b are never read
  *   seqlens    [B] int32 device array of cache lengths, 4-byte aligned, or
  *              NULL for S_max everywhere.  A length above S_max counts as
  *              S_max; a length <= 0 gives out = 0 and lse = -inf.
- *   out        [B, H_q, d] bf16 output, 16-byte aligned
+ *   out        [B, H_q, d] output of `dtype`, 16-byte aligned
  *   lse        [B, H_q] fp32 output (natural log), 4-byte aligned, or NULL
  *   workspace  caller-owned device scratch of at least
  *              sqa_attn_decode_workspace_size(...) bytes, 16-byte aligned;
@@ -172,10 +172,11 @@ int64_t sqa_attn_bwd_workspace_size(int64_t B, int64_t S, int32_t H_q);
  *
  * Outputs and workspace must not overlap each other or any input.
  * SQA_ERR_INVALID_ARGUMENT as for sqa_attn_fwd (and for a short workspace);
- * SQA_ERR_UNSUPPORTED for dtype SQA_FP32, d not in {32, 64, 128} or
- * S_max > 2^30.  B == 0 is a successful no-op.  Asynchronous on `stream`:
- * a split kernel (bf16 MFMA, fp32 accumulation, probabilities rounded to
- * bf16 for the P.V product) and a combine kernel.
+ * SQA_ERR_UNSUPPORTED for d not in {32, 64, 128} or S_max > 2^30.  B == 0
+ * is a successful no-op.  Asynchronous on `stream`.  bf16: a split kernel
+ * (bf16 MFMA, fp32 accumulation, probabilities rounded to bf16 for the P.V
+ * product) and a combine kernel; fp32: a plain fp32 kernel (one thread per
+ * sequence and head, workspace unused) for exactness checks at small sizes.
  */
 sqa_status sqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
                            void* out, float* lse, void* workspace, int64_t workspace_bytes, int64_t B,

@@ -199,7 +199,7 @@ def attn_decode(q, k_cache, v_cache, seqlens=None, out=None, scale=None, stream=
                 workspace=None):
     """One query token per sequence against its key/value cache.
 
-    q: [B, H_q, d] bfloat16; k_cache, v_cache: [B, S_max, H_kv, d] bfloat16;
+    q: [B, H_q, d]; k_cache, v_cache: [B, S_max, H_kv, d]; all bfloat16 or all float32;
     seqlens: int32 [B] GPU tensor of cache lengths (None = S_max).  Returns
     out [B, H_q, d] (and the fp32 [B, H_q] log-normaliser with return_lse).
     A uint8 workspace of attn_decode_workspace_size(...) bytes is allocated
@@ -208,8 +208,11 @@ def attn_decode(q, k_cache, v_cache, seqlens=None, out=None, scale=None, stream=
     import torch
 
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
-        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
-            raise ValueError(f"{name} must be a contiguous bfloat16 GPU tensor")
+        if not t.is_cuda or not t.is_contiguous() or t.dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError(f"{name} must be a contiguous bfloat16 or float32 GPU tensor")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q, k_cache, v_cache must share one dtype")
+    dtype = SQA_BF16 if q.dtype == torch.bfloat16 else SQA_FP32
     if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
         raise ValueError(f"expected q [B,H_q,d], caches [B,S_max,H_kv,d]; got q{tuple(q.shape)} "
                          f"k{tuple(k_cache.shape)} v{tuple(v_cache.shape)}")
@@ -241,7 +244,7 @@ def attn_decode(q, k_cache, v_cache, seqlens=None, out=None, scale=None, stream=
     st = attn_decode_raw(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                          seqlens.data_ptr() if seqlens is not None else None, out.data_ptr(),
                          lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
-                         workspace.numel() * workspace.element_size(), B, S_max, H_q, H_kv, d, SQA_BF16,
+                         workspace.numel() * workspace.element_size(), B, S_max, H_q, H_kv, d, dtype,
                          float(scale), handle)
     if st != SQA_OK:
         raise SqaError(st, status_string(st))

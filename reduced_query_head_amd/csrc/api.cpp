@@ -219,9 +219,8 @@ SQA_API sqa_status sqa_attn_decode(const void* q, const void* k_cache, const voi
     for (int j = i + 1; j < 3; ++j)
       if (outs[j] && ranges_overlap(outs[i], out_bytes[i], outs[j], out_bytes[j])) return SQA_ERR_INVALID_ARGUMENT;
   }
-  if (dtype != SQA_BF16) return SQA_ERR_UNSUPPORTED;
   if (d != 32 && d != 64 && d != 128) return SQA_ERR_UNSUPPORTED;
-  if ((plan.n_waves + 3) / 4 > INT32_MAX || (B * H_q + 3) / 4 > INT32_MAX) return SQA_ERR_UNSUPPORTED;
+  if ((plan.n_waves + 3) / 4 > INT32_MAX || (B * H_q + 255) / 256 > INT32_MAX) return SQA_ERR_UNSUPPORTED;
 
   sqa::DecodeArgs a;
   a.q = q;
@@ -236,6 +235,7 @@ SQA_API sqa_status sqa_attn_decode(const void* q, const void* k_cache, const voi
   a.H_q = H_q;
   a.H_kv = H_kv;
   a.d = d;
+  a.dtype = dtype == SQA_BF16 ? 0 : 1;
   const float log2e = 1.4426950408889634f;
   const float mag = fabsf(scale);
   a.c = mag > 0.f ? mag * log2e : 1e-30f;

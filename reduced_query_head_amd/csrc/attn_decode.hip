@@ -26,6 +26,7 @@
 //    and writes the bf16 output and lse = ln2 (M + log2 L).
 // Cache lengths come from a device array (or are all S_max); a length above
 // S_max counts as S_max, and an empty cache gives out = 0, lse = -inf.
+// fp32 inputs take a plain one-thread-per-(b, h) kernel (exactness checks).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -305,6 +306,66 @@ __global__ __launch_bounds__(256) void attn_decode_combine_bf16(DecodeParams p) 
   }
 }
 
+// fp32 path: one thread per (b, h), online softmax over the cache in fp32.
+// Plain VALU arithmetic for exactness checks at small sizes.
+template <int D>
+__global__ __launch_bounds__(256) void attn_decode_f32(const float* __restrict__ q, const float* __restrict__ k,
+                                                       const float* __restrict__ v, const int32_t* __restrict__ seqlens,
+                                                       float* __restrict__ out, float* __restrict__ lse, int64_t B,
+                                                       int S_max, int H_q, int H_kv, int R, float c) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= B * H_q) return;
+  const int64_t b = t / H_q;
+  const int h = (int)(t % H_q);
+  const int g = h / R;
+  int len = seqlens ? seqlens[b] : S_max;
+  len = min(len, S_max);
+  float* op = out + t * D;
+  if (len <= 0) {
+#pragma unroll
+    for (int e = 0; e < D; ++e) op[e] = 0.f;
+    if (lse) lse[t] = -__builtin_inff();
+    return;
+  }
+  float qv[D], acc[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    qv[e] = q[t * D + e];
+    acc[e] = 0.f;
+  }
+  float m = -__builtin_inff(), l = 0.f;
+  for (int j = 0; j < len; ++j) {
+    const float* kp = k + ((b * S_max + j) * H_kv + g) * D;
+    const float* vp = v + ((b * S_max + j) * H_kv + g) * D;
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < D; ++e) dot = __builtin_fmaf(qv[e], kp[e], dot);
+    const float x = dot * c;
+    const float m_new = fmaxf(m, x);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    const float pj = __builtin_amdgcn_exp2f(x - m_new);
+    m = m_new;
+    l = l * alpha + pj;
+#pragma unroll
+    for (int e = 0; e < D; ++e) acc[e] = __builtin_fmaf(pj, vp[e], acc[e] * alpha);
+  }
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int e = 0; e < D; ++e) op[e] = acc[e] * inv;
+  if (lse) lse[t] = (m + log2f(l)) * 0.69314718055994531f;
+}
+
+template <int D>
+hipError_t launch_decode_f32_t(const DecodeArgs& a) {
+  const int64_t threads = a.B * a.H_q;
+  // the fp32 kernel keeps the sign of the scale in c (no bf16 operand to negate)
+  const float c = a.negate_q ? -a.c : a.c;
+  hipLaunchKernelGGL((attn_decode_f32<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     (hipStream_t)a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v, a.seqlens,
+                     (float*)a.out, a.lse, a.B, (int)a.S_max, a.H_q, a.H_kv, a.H_q / a.H_kv, c);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& plan) {
   DecodeParams p;
@@ -363,6 +424,14 @@ DecodePlan decode_plan(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int3
 }
 
 hipError_t launch_attn_decode(const DecodeArgs& a) {
+  if (a.dtype == 1) {
+    switch (a.d) {
+      case 32: return launch_decode_f32_t<32>(a);
+      case 64: return launch_decode_f32_t<64>(a);
+      case 128: return launch_decode_f32_t<128>(a);
+    }
+    return hipErrorInvalidValue;
+  }
   const DecodePlan plan = decode_plan(a.B, a.S_max, a.H_q, a.H_kv, a.d);
   switch (a.d) {
     case 32: return launch_decode_t<32>(a, plan);

@@ -71,6 +71,7 @@ struct DecodeArgs {
   int32_t H_q;
   int32_t H_kv;
   int32_t d;
+  int dtype;              // 0 = bf16, 1 = fp32
   float c;                // |scale| * log2(e), or a tiny positive value when scale == 0
   bool negate_q;          // scale < 0
   void* stream;

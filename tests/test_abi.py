@@ -164,7 +164,7 @@ def test_decode_invalid(kw):
     assert _call_dec(**kw) == sqa.SQA_ERR_INVALID_ARGUMENT
 
 
-@pytest.mark.parametrize("kw", [dict(dtype=1), dict(d=96), dict(d=16), dict(d=256)])
+@pytest.mark.parametrize("kw", [dict(d=96), dict(d=16), dict(d=256), dict(dtype=1, d=96)])
 def test_decode_unsupported(kw):
     assert _call_dec(**kw) == sqa.SQA_ERR_UNSUPPORTED
 

@@ -159,3 +159,22 @@ def test_decode_full_size(variant):
     out, lse = _run(q, k, v, lens, w.scale)
     st = _check(out, lse, q, k, v, lens, w.scale, f"{w.name}/{variant}")
     _say(f"  {st}")
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_decode_f32(d):
+    """fp32 path against the oracle at the fp32 bounds (max 1e-4, relative L2 1e-5)."""
+    B, S_max, H_q, H_kv = 3, 300, 8, 2
+    q = inputs.normal(80 + d, 0, (B, H_q, d), "f32")
+    k = inputs.normal(80 + d, 1, (B, S_max, H_kv, d), "f32")
+    v = inputs.normal(80 + d, 2, (B, S_max, H_kv, d), "f32")
+    lens = [300, 1, 0]
+    dq, dk, dv = gpu_util.to_device(q), gpu_util.to_device(k), gpu_util.to_device(v)
+    dl = torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
+    out, lse = sqa.attn_decode(dq, dk, dv, seqlens=dl, scale=-1 / math.sqrt(d), return_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.decode(q, k, v, float(np.float32(-1 / math.sqrt(d))), seqlens=lens)
+    got = out.double().cpu().numpy()
+    assert (got[2] == 0).all() and np.isneginf(lse[2].cpu().numpy()).all()
+    parity.check(got[:2], ref[:2], "f32", f"decode f32 d={d}")
+    assert np.abs(lse[:2].double().cpu().numpy() - ref_lse[:2]).max() < 2e-5
