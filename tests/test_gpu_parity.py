@@ -71,6 +71,24 @@ def test_scale_values(scale):
         check(got, ref, "bf16", f"scale={scale} causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_sharp_softmax(causal):
+    """N(0,1) inputs with scale 0.7 at d = 128: scaled scores have a standard
+    deviation near 8, so each row's softmax is dominated by a few keys and any
+    error in the scores themselves (for instance q * scale rounded to bf16
+    before the product, ~6e-2 max error here) shows directly in the output.
+    With exact fp32 scores only the bf16 rounding of the probabilities and of
+    the output remains (~9e-3 max, ~9e-4 mean in an fp64 model of it)."""
+    B, S, H_q, H_kv, d = 1, 1024, 4, 2, 128
+    q = inputs.normal(56, 0, (B, S, H_q, d), "bf16", 1.0)
+    k = inputs.normal(56, 1, (B, S, H_kv, d), "bf16", 1.0)
+    v = inputs.normal(56, 2, (B, S, H_kv, d), "bf16", 1.0)
+    got = gpu_util.to_host_f64(gpu_util.run(q, k, v, 0.7, causal))
+    ref = oracle.attention(q, k, v, float(np.float32(0.7)), causal=causal)
+    st = check(got, ref, "bf16", f"sharp softmax causal={causal}")
+    _say(f"  {st}")
+
+
 def test_tiny_f32_workload_full():
     w = WORKLOADS["tiny_f32"]
     _say("workload tiny_f32")
