@@ -220,7 +220,9 @@ SQA_API sqa_status sqa_attn_decode(const void* q, const void* k_cache, const voi
       if (outs[j] && ranges_overlap(outs[i], out_bytes[i], outs[j], out_bytes[j])) return SQA_ERR_INVALID_ARGUMENT;
   }
   if (d != 32 && d != 64 && d != 128) return SQA_ERR_UNSUPPORTED;
-  if ((plan.n_waves + 3) / 4 > INT32_MAX || (B * H_q + 255) / 256 > INT32_MAX) return SQA_ERR_UNSUPPORTED;
+  // split grid (4 waves per workgroup), combine grid (d/32 workgroups per row), fp32 grid
+  if ((plan.n_waves + 3) / 4 > INT32_MAX || B * H_q * (d / 32) > INT32_MAX || (B * H_q + 255) / 256 > INT32_MAX)
+    return SQA_ERR_UNSUPPORTED;
 
   sqa::DecodeArgs a;
   a.q = q;

@@ -21,9 +21,10 @@
 //    one block ahead, so each wave keeps about 24 KiB of cache reads in
 //    flight.  Each writes the split's running maximum m (log2 units), row sum
 //    l and unnormalised O^T to a workspace.
-//  * attn_decode_combine: one workgroup per (b, h) merges the splits of that
-//    head: M = max m_s, L = sum l_s 2^(m_s - M), O = sum O_s 2^(m_s - M) / L,
-//    and writes the bf16 output and lse = ln2 (M + log2 L).
+//  * attn_decode_combine: one workgroup per (b, h, 32 head dims) merges the
+//    splits of that head: M = max m_s, L = sum l_s 2^(m_s - M),
+//    O = sum O_s 2^(m_s - M) / L, and writes the bf16 output and
+//    lse = ln2 (M + log2 L).
 // Cache lengths come from a device array (or are all S_max); a length above
 // S_max counts as S_max, and an empty cache gives out = 0, lse = -inf.
 // fp32 inputs take a plain one-thread-per-(b, h) kernel (exactness checks).
@@ -240,13 +241,14 @@ __global__ __launch_bounds__(kWavesDec * 64, 2) void attn_decode_split_bf16(Deco
           (f32x4){o[db][4 * j], o[db][4 * j + 1], o[db][4 * j + 2], o[db][4 * j + 3]};
 }
 
-// One workgroup per (b, h): merge the non-empty splits of that head.  The
-// 256 threads form SG split groups of D/4 lanes, each lane holding 4 head
-// dims (16-byte loads); a maximum pass over the splits, a weighted-sum pass,
-// then an LDS reduction over the split groups.
+// One workgroup per (b, h, 32-dim chunk): merge the non-empty splits of that
+// head for 32 of its head dims.  The 256 threads form 32 split groups of 8
+// lanes, each lane holding 4 head dims (16-byte loads); a maximum pass over
+// the splits, a weighted-sum pass, then an LDS reduction over the groups.
 template <int D>
 __global__ __launch_bounds__(256) void attn_decode_combine_bf16(DecodeParams p) {
-  constexpr int LANES = D / 4;          // lanes per split group
+  constexpr int DC = D / 32;            // dim chunks per head
+  constexpr int LANES = 8;              // lanes per split group
   constexpr int SG = 256 / LANES;       // split groups
   __shared__ float red_m[4];
   __shared__ float red_l[SG];
@@ -256,18 +258,19 @@ __global__ __launch_bounds__(256) void attn_decode_combine_bf16(DecodeParams p) 
   const int wave = tid >> 6;
   const int grp = tid / LANES;
   const int dl = tid % LANES;
-  const int64_t row = blockIdx.x;      // b * H_q + h
+  const int64_t row = blockIdx.x / DC;      // b * H_q + h
+  const int dc = blockIdx.x % DC;
   const int b = (int)(row / p.H_q);
   const int len = cache_len(p, b);
-  uint16_t* op = p.out + row * D;
+  uint16_t* op = p.out + row * D + dc * 32;
   if (len <= 0) {   // uniform over the workgroup
-    if (tid < D) op[tid] = 0;
-    if (p.lse && tid == 0) p.lse[row] = -__builtin_inff();
+    if (tid < 32) op[tid] = 0;
+    if (p.lse && dc == 0 && tid == 0) p.lse[row] = -__builtin_inff();
     return;
   }
   const int n_valid = (len + p.split_len - 1) / p.split_len;
   const float* ml = p.part_ml + row * p.n_splits * 2;
-  const float* po = p.part_o + row * p.n_splits * D;
+  const float* po = p.part_o + row * p.n_splits * D + dc * 32;
 
   float M = -__builtin_inff();
   for (int s = tid; s < n_valid; s += 256) M = fmaxf(M, ml[2 * s]);
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(256) void attn_decode_combine_bf16(DecodeParams p) 
 #pragma unroll
     for (int e = 0; e < 4; ++e) w4[e] = (__bf16)(o[e] * inv);
     *(bf16x4*)(op + tid * 4) = w4;
-    if (p.lse && tid == 0) p.lse[row] = (M + log2f(Lt)) * 0.69314718055994531f;
+    if (p.lse && dc == 0 && tid == 0) p.lse[row] = (M + log2f(Lt)) * 0.69314718055994531f;
   }
 }
 
@@ -393,7 +396,8 @@ hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& plan) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = a.B * a.H_q;
-  hipLaunchKernelGGL((attn_decode_combine_bf16<D>), dim3((unsigned)rows), dim3(256), 0, (hipStream_t)a.stream, p);
+  hipLaunchKernelGGL((attn_decode_combine_bf16<D>), dim3((unsigned)(rows * (D / 32))), dim3(256), 0,
+                     (hipStream_t)a.stream, p);
   return hipGetLastError();
 }
 
