@@ -216,16 +216,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdParams p) {
     lds_mfma_pipeline_hint<2 * KS * NB, 1, 4>();
     // P = 2^(c s - lse2), masked keys 0; dS = P (dP - D); key of s[nb][r] is
     // kv0 + 4*half + nb*32 + 8*(r/4) + r%4
+    // masked scores go to -inf (P = 0) in a pass of their own, taken only on
+    // tiles that hold a masked key
     const bool need_mask = (kv0 + KEYS > S) || (CAUSAL && kv0 + KEYS - 1 > pos0);
-    const int lim = (CAUSAL ? min(my_q, S - 1) : S - 1) - kv0 - 4 * half;
+    if (__builtin_expect(need_mask, 0)) {
+      asm volatile("" ::: "memory");  // keeps this pass a branch (no if-conversion into selects)
+      const int lim = (CAUSAL ? min(my_q, S - 1) : S - 1) - kv0 - 4 * half;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (nb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[nb][r] = -__builtin_inff();
+    }
     bf16x8 dsk[NT];
 #pragma unroll
     for (int st = 0; st < NT; ++st)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int nb = st >> 1, r = (st & 1) * 8 + e;
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][r], c, -lse2));
-        if (need_mask && (nb * 32 + 8 * (r >> 2) + (r & 3) > lim)) pv = 0.f;
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][r], c, -lse2));
         dsk[st][e] = (__bf16)(pv * (dp[nb][r] - delta));
       }
     // dQ^T += K^T dS^T (K^T from transposing reads of the K tile)
@@ -417,15 +426,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
       const int qbase = q0 + qh * 32;
       // rows past S have lse2 = +inf (P = 0); only the causal mask is explicit
       const bool need_mask = CAUSAL && qbase < key0 + 31;
-      const int qlo = qbase + 4 * half;
+      if (__builtin_expect(need_mask, 0)) {
+        asm volatile("" ::: "memory");  // keeps this pass a branch
+        const int qlo = qbase + 4 * half;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (my_key > qlo + 8 * (r >> 2) + (r & 3)) s[qh][r] = -__builtin_inff();
+      }
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = st * 8 + e;
-          const int qi = qlo + 8 * (r >> 2) + (r & 3);
-          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qh][r], c, -l2[r]));
-          if (need_mask && my_key > qi) pv = 0.f;
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qh][r], c, -l2[r]));
           pk[qh][st][e] = (__bf16)pv;
           dsk[qh][st][e] = (__bf16)(pv * (dp[qh][r] - dl[r]));
         }
