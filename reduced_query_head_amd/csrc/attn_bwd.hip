@@ -11,7 +11,9 @@
 // the query heads of a group.  Three kernels:
 //
 //  * bwd_stats: D_i = <dO_i, O_i> and lse_i * log2(e), written per (b, head)
-//    as contiguous, 64-padded rows of a caller-provided workspace.
+//    as contiguous, 64-padded rows of a caller-provided workspace, negated and
+//    (lse) divided by c, so that the dK/dV kernel can start its score and dP
+//    accumulators at them.
 //  * bwd_dq: one wave per 32 query rows of one head; K/V tiles of 64 keys
 //    staged in LDS for the whole K/V group (as in the forward).  With keys
 //    along MFMA M (S^T = K Q^T, dP^T = V dO^T) each lane owns one query, so
@@ -22,10 +24,12 @@
 //    their statistics) of all R query heads of the group stream through LDS.
 //    S = Q K^T and dP = dO V^T put keys on lanes, so dV^T += dO^T P and
 //    dK^T += Q^T dS take P and dS straight from the accumulators and dO^T,
-//    Q^T from transposing LDS reads.  The two 32-query halves of a tile form
-//    a two-stage pipeline in the instruction stream (half 1's products
-//    between half 0's softmax instructions and so on), since no second wave
-//    on the SIMD can fill the gaps.
+//    Q^T from transposing LDS reads.  The accumulators start at
+//    -lse_i*log2(e)/c and -D_i, so they end at s - lse2/c and dP - D:
+//    P = 2^(c acc) and dS = P acc' with no per-score subtraction.  The two
+//    32-query halves of a tile form a two-stage pipeline in the instruction
+//    stream (half 1's products between half 0's softmax instructions and so
+//    on), since no second wave on the SIMD can fill the gaps.
 //
 // All matrix products are bf16 MFMA with fp32 accumulation; P and dS are
 // rounded to bf16 for the products that consume them.  The fp32 path is plain
@@ -54,8 +58,8 @@ struct BwdParams {
   const uint16_t* o;
   const uint16_t* dout;
   const float* lse;
-  float* ws_lse2;    // [B, H_q, S_pad]: lse * log2(e)
-  float* ws_delta;   // [B, H_q, S_pad]: <dO_i, O_i>
+  float* ws_lse2;    // [B, H_q, S_pad]: -lse * log2(e) / c  (pad rows -inf)
+  float* ws_delta;   // [B, H_q, S_pad]: -<dO_i, O_i>        (pad rows 0)
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -107,10 +111,13 @@ __global__ __launch_bounds__(256) void bwd_stats_bf16(BwdParams p, int64_t B) {
   acc += __shfl_xor(acc, 4);
   if (row < total && sub == 0) {
     const bool valid = i < p.S;
-    p.ws_delta[row] = valid ? acc : 0.f;
-    // pad rows get lse2 = +inf, so their probabilities 2^(c s - lse2) are
-    // exactly 0 wherever they are recomputed (no per-element tail mask)
-    p.ws_lse2[row] = valid ? p.lse[(b * p.S + i) * p.H_q + h] * 1.4426950408889634f : __builtin_inff();
+    // stored negated and (for lse) divided by c: they are the initial values
+    // of the dK/dV kernel's score and dP accumulators, which then hold
+    // s - lse2/c and dP - D directly.  Pad rows get -inf, so their
+    // probabilities 2^(c (s - lse2/c)) are exactly 0 wherever they are
+    // recomputed (no per-element tail mask).
+    p.ws_delta[row] = valid ? -acc : 0.f;
+    p.ws_lse2[row] = valid ? -(p.lse[(b * p.S + i) * p.H_q + h] * 1.4426950408889634f) / p.c : -__builtin_inff();
   }
 }
 
@@ -168,8 +175,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdParams p) {
     }
   }
   const int64_t srow = ((int64_t)b * p.H_q + h) * p.S_pad + qrow;
-  const float lse2 = p.ws_lse2[srow];
-  const float delta = p.ws_delta[srow];
+  const float lse2 = -p.c * p.ws_lse2[srow];   // the workspace holds -lse2/c and -D
+  const float delta = -p.ws_delta[srow];
 
   int k_off[KS];
 #pragma unroll
@@ -396,14 +403,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
         }
       }
     };
-    float l2a[16], dla[16];
-    load_stats(0, l2a, dla);
-    // S = Q K^T and dP = dO V^T (queries along M, this lane's key along N)
+    // S - lse2/c = Q K^T + (-lse2/c) and dP - D = dO V^T + (-D): the row
+    // statistics (stored negated, lse2 divided by c) start the accumulators
+    // (queries along M, this lane's key along N)
     f32x16 s[NH], dp[NH];
 #pragma unroll
     for (int qh = 0; qh < NH; ++qh) {
-      s[qh] = (f32x16){};
-      dp[qh] = (f32x16){};
+      float l2[16], dl[16];
+      load_stats(qh, l2, dl);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[qh][r] = l2[r];
+        dp[qh][r] = dl[r];
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 a = *(const SQA_LDS bf16x8*)(qt_l + qh * 32 * D + a_off[ks]);
@@ -419,12 +431,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
     bf16x8 pk[NH][2], dsk[NH][2];
 #pragma unroll
     for (int qh = 0; qh < NH; ++qh) {
-      float l2b[16], dlb[16];
-      if (qh == 1) load_stats(1, l2b, dlb);
-      const float* l2 = qh == 0 ? l2a : l2b;
-      const float* dl = qh == 0 ? dla : dlb;
       const int qbase = q0 + qh * 32;
-      // rows past S have lse2 = +inf (P = 0); only the causal mask is explicit
+      // the accumulators of rows past S start at -inf (P = 0); only the causal mask is explicit
       const bool need_mask = CAUSAL && qbase < key0 + 31;
       if (__builtin_expect(need_mask, 0)) {
         asm volatile("" ::: "memory");  // keeps this pass a branch
@@ -438,9 +446,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = st * 8 + e;
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qh][r], c, -l2[r]));
+          const float pv = __builtin_amdgcn_exp2f(s[qh][r] * c);
           pk[qh][st][e] = (__bf16)pv;
-          dsk[qh][st][e] = (__bf16)(pv * (dp[qh][r] - dl[r]));
+          dsk[qh][st][e] = (__bf16)(pv * dp[qh][r]);
         }
     }
     // dV^T += dO^T P and dK^T += Q^T dS (16 queries per MFMA step)
@@ -463,7 +471,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
     // instruction order: half-0 stats and S/dP reads; half-0 S/dP; half-1 S/dP
     // with half-0 softmax; half-0 dV/dK with half-1 softmax; half-1 dV/dK
     static_assert(NH == 2, "the schedule below is written for two query halves");
-    __builtin_amdgcn_sched_group_barrier(0x100, 8 + 8, 0);
+    // both halves' row statistics (8 reads each) and the first operands up
+    // front when non-causal; the causal kernel measured faster taking half
+    // 1's statistics in the reads that follow
+    __builtin_amdgcn_sched_group_barrier(0x100, CAUSAL ? 8 + 8 : 8 + 8 + 8, 0);
 #pragma unroll
     for (int i = 0; i < 2 * KS - 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
