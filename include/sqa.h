@@ -73,6 +73,7 @@ typedef enum {
  *   H_q, H_kv  query and key/value head counts: H_q >= H_kv >= 1 and
  *              H_q % H_kv == 0
  *   d          head dimension: 32, 64 or 128
+ *              (H_q * d and H_kv * d at most 2^22: UNSUPPORTED beyond)
  *   scale      finite multiplier of the scores (1/sqrt(d) is usual)
  *   causal     0 = every query sees all S keys; 1 = query i sees keys j <= i
  *   stream     HIP stream to enqueue on (NULL = null stream)
@@ -131,8 +132,7 @@ sqa_status sqa_attn_fwd_lse(const void* q, const void* k, const void* v, void* o
  *                        forward that produced out and lse)
  *
  * Outputs and workspace must not overlap each other or any input.  Errors as
- * for sqa_attn_fwd; SQA_ERR_UNSUPPORTED also when the workspace would reach
- * 4 GiB.  bf16: MFMA kernels with fp32 accumulation, probabilities and dS
+ * for sqa_attn_fwd.  bf16: MFMA kernels with fp32 accumulation, probabilities and dS
  * rounded to bf16 for the products; fp32: plain fp32 arithmetic.
  */
 sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -172,7 +172,8 @@ int64_t sqa_attn_bwd_workspace_size(int64_t B, int64_t S, int32_t H_q);
  *
  * Outputs and workspace must not overlap each other or any input.
  * SQA_ERR_INVALID_ARGUMENT as for sqa_attn_fwd (and for a short workspace);
- * SQA_ERR_UNSUPPORTED for d not in {32, 64, 128} or S_max > 2^30.  B == 0
+ * SQA_ERR_UNSUPPORTED for d not in {32, 64, 128}, H_q * d or H_kv * d above
+ * 2^22, or S_max > 2^30.  B == 0
  * is a successful no-op.  Asynchronous on `stream`.  bf16: a split kernel
  * (bf16 MFMA, fp32 accumulation, probabilities rounded to bf16 for the P.V
  * product) and a combine kernel; fp32: a plain fp32 kernel (one thread per
@@ -215,8 +216,8 @@ int64_t sqa_attn_decode_workspace_size(int64_t B, int64_t S_max, int32_t H_q, in
  * attention output before the output projection.  out must not overlap any
  * input or the workspace; the workspace must not overlap any input.
  * SQA_ERR_INVALID_ARGUMENT as for sqa_attn_fwd (also d_model < 1 or a short
- * workspace); SQA_ERR_UNSUPPORTED for d not in {32, 64, 128}, d_model not a
- * multiple of 8 or S > 2^30; SQA_ERR_HIP for a HIP or hipBLASLt failure.
+ * workspace); SQA_ERR_UNSUPPORTED for d not in {32, 64, 128},
+ * (H_q + 2 H_kv) * d above 2^22, d_model not a multiple of 8 or S > 2^30; SQA_ERR_HIP for a HIP or hipBLASLt failure.
  */
 sqa_status sqa_layer_fwd(const void* x, const void* w_qkv, const void* w_o, void* out, void* workspace,
                          int64_t workspace_bytes, int64_t B, int64_t S, int32_t d_model, int32_t H_q, int32_t H_kv,

@@ -22,6 +22,13 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   return true;
 }
 
+// Kernels address a tile of up to 128 rows relative to a 64-bit tile base
+// with 32-bit byte offsets: rows of up to 2^22 elements (32768 heads at
+// d = 128) keep those under 1 GiB.
+constexpr int64_t kMaxRowElems = (int64_t)1 << 22;
+
+bool row_ok(int64_t heads, int32_t d) { return heads * d <= kMaxRowElems; }
+
 }  // namespace
 
 SQA_API const char* sqa_status_string(sqa_status status) {
@@ -67,6 +74,7 @@ SQA_API sqa_status sqa_attn_fwd_lse(const void* q, const void* k, const void* v,
   }
 
   if (d != 32 && d != 64 && d != 128) return SQA_ERR_UNSUPPORTED;
+  if (!row_ok(H_q, d) || !row_ok(H_kv, d)) return SQA_ERR_UNSUPPORTED;
   // kernels index positions with 32-bit integers
   if (S > (int64_t)1 << 30) return SQA_ERR_UNSUPPORTED;
   if (dtype == SQA_BF16) {
@@ -146,9 +154,8 @@ SQA_API sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, con
       if (ranges_overlap(outs[i], out_bytes[i], outs[j], out_bytes[j])) return SQA_ERR_INVALID_ARGUMENT;
   }
   if (d != 32 && d != 64 && d != 128) return SQA_ERR_UNSUPPORTED;
+  if (!row_ok(H_q, d) || !row_ok(H_kv, d)) return SQA_ERR_UNSUPPORTED;
   if (S > (int64_t)1 << 30) return SQA_ERR_UNSUPPORTED;
-  // the statistics copies address the workspace with 32-bit byte offsets
-  if (ws_need >= ((int64_t)1 << 32)) return SQA_ERR_UNSUPPORTED;
   if (dtype == SQA_BF16 ? sqa::bwd_grid_size(B, S, H_q, H_kv) > INT32_MAX
                         : (rows * H_q + 255) / 256 > INT32_MAX)
     return SQA_ERR_UNSUPPORTED;
@@ -220,6 +227,7 @@ SQA_API sqa_status sqa_attn_decode(const void* q, const void* k_cache, const voi
       if (outs[j] && ranges_overlap(outs[i], out_bytes[i], outs[j], out_bytes[j])) return SQA_ERR_INVALID_ARGUMENT;
   }
   if (d != 32 && d != 64 && d != 128) return SQA_ERR_UNSUPPORTED;
+  if (!row_ok(H_q, d) || !row_ok(H_kv, d)) return SQA_ERR_UNSUPPORTED;
   // split grid (4 waves per workgroup), combine grid (d/32 workgroups per row), fp32 grid
   if ((plan.n_waves + 3) / 4 > INT32_MAX || B * H_q * (d / 32) > INT32_MAX || (B * H_q + 255) / 256 > INT32_MAX)
     return SQA_ERR_UNSUPPORTED;
@@ -250,7 +258,7 @@ SQA_API sqa_status sqa_attn_decode(const void* q, const void* k_cache, const voi
 SQA_API int64_t sqa_layer_workspace_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv, int32_t d) {
   if (B < 0 || S < 0 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || d < 1) return -1;
   int64_t rows, t;
-  if (!mul_ok(B, S, &rows) || !mul_ok(rows, (int64_t)(H_q + 2 * H_kv) * d * 4, &t)) return -1;
+  if (!mul_ok(B, S, &rows) || !mul_ok(rows, ((int64_t)H_q + 2 * (int64_t)H_kv) * d * 4, &t)) return -1;
   return sqa::layer_plan(B, S, H_q, H_kv, d).workspace_bytes;
 }
 
@@ -266,7 +274,7 @@ SQA_API sqa_status sqa_layer_fwd(const void* x, const void* w_qkv, const void* w
   if (((uintptr_t)x | (uintptr_t)w_qkv | (uintptr_t)w_o | (uintptr_t)out | (uintptr_t)workspace) & 15u)
     return SQA_ERR_INVALID_ARGUMENT;
   int64_t rows, x_bytes, wqkv_bytes, wo_bytes, ws_probe;
-  const int64_t n_qkv = (int64_t)(H_q + 2 * H_kv) * d;
+  const int64_t n_qkv = ((int64_t)H_q + 2 * (int64_t)H_kv) * d;
   if (!mul_ok(B, S, &rows) || !mul_ok(rows, (int64_t)d_model * 2, &x_bytes) ||
       !mul_ok(n_qkv, (int64_t)d_model * 2, &wqkv_bytes) || !mul_ok((int64_t)H_q * d, (int64_t)d_model * 2, &wo_bytes) ||
       !mul_ok(rows, n_qkv * 4, &ws_probe))   // the workspace sizes stay representable
@@ -281,6 +289,7 @@ SQA_API sqa_status sqa_layer_fwd(const void* x, const void* w_qkv, const void* w
       return SQA_ERR_INVALID_ARGUMENT;
   if (ranges_overlap(out, x_bytes, workspace, lp.workspace_bytes)) return SQA_ERR_INVALID_ARGUMENT;
   if (d != 32 && d != 64 && d != 128) return SQA_ERR_UNSUPPORTED;
+  if (!row_ok((int64_t)H_q + 2 * (int64_t)H_kv, d)) return SQA_ERR_UNSUPPORTED;
   // rows of x, W_qkv and W_o must stay 16-byte aligned for the GEMM library
   if (d_model % 8 != 0) return SQA_ERR_UNSUPPORTED;
   if (S > (int64_t)1 << 30 || sqa::bf16_grid_size(B, S, H_q, H_kv) > INT32_MAX) return SQA_ERR_UNSUPPORTED;

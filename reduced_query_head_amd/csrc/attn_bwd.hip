@@ -278,8 +278,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dK, dV: 4 waves per workgroup, 32 keys per wave (128 keys per workgroup).
 // Copies of one query tile: Q rows and dO rows of head h (TileCopy), plus
-// 256-byte runs of lse2 and delta: lanes 0-15 and 16-31 of one extra copy
-// (lanes 32-63 repeat the lse2 run into the unused upper half).
+// the 256-byte runs of lse2 and delta, one copy each from its own 64-bit base
+// (lanes 0-15 carry the run; the others repeat it into unused LDS).
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
   constexpr int WAVES = kWaves, QT = kTile;
@@ -290,8 +290,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds_q1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_g0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_g1[TILE];
-  __shared__ __attribute__((aligned(1024))) float lds_s0[256];  // [0,64) lse2, [64,128) delta
-  __shared__ __attribute__((aligned(1024))) float lds_s1[256];
+  __shared__ __attribute__((aligned(1024))) float lds_s0[512];  // [0,64) lse2, [256,320) delta
+  __shared__ __attribute__((aligned(1024))) float lds_s1[512];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_kk[KEYS_WG * D];   // this workgroup's K rows
   __shared__ __attribute__((aligned(1024))) uint16_t lds_vv[KEYS_WG * D];   // and V rows
 
@@ -317,10 +317,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
   const int64_t q_stride = (int64_t)p.H_q * D;
   TileCopy<D, WAVES, QT> cp;
   cp.init(q_stride, wave, lane);
-  // per-lane stats copy offset (bytes from ws base) for the tile of (h, qt)
-  const float* ws = p.ws_lse2;
-  const uint32_t delta_shift = (uint32_t)((p.ws_delta - p.ws_lse2) * 4);
-  const uint32_t stat_lane = lane < 16 ? lane * 16u : lane < 32 ? delta_shift + (lane - 16) * 16u : (lane & 15) * 16u;
+  // statistics of a tile: two 256-byte runs (lse2, delta) at 64-bit bases;
+  // lanes 16-63 repeat lanes 0-15 into the unused rest of each 1 KiB half
+  const uint32_t stat_lane = (uint32_t)(lane & 15) * 16u;
 
   auto issue_tile = [&](int u, SQA_LDS uint16_t* qd, SQA_LDS uint16_t* gd, SQA_LDS float* sd) {
     const int hl = u / qt_count;
@@ -331,7 +330,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
     cp.issue(p.dout + base, q_stride, S - qt * QT, gd, wave);
     if (wave == 0) {
       const int64_t srow = ((int64_t)b * p.H_q + h) * p.S_pad + qt * QT;
-      dma16(ws, (uint32_t)(srow * 4) + stat_lane, lds_addr(sd));
+      dma16(p.ws_lse2 + srow, stat_lane, lds_addr(sd));
+      dma16(p.ws_delta + srow, stat_lane, lds_addr(sd + 256));
     }
   };
 
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x4 a = *(const SQA_LDS f32x4*)(st_l + qh * 32 + 8 * j + 4 * half);
-        const f32x4 d4 = *(const SQA_LDS f32x4*)(st_l + 64 + qh * 32 + 8 * j + 4 * half);
+        const f32x4 d4 = *(const SQA_LDS f32x4*)(st_l + 256 + qh * 32 + 8 * j + 4 * half);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           l2[4 * j + e] = a[e];

@@ -97,7 +97,7 @@ int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 LayerPlan layer_plan(int64_t B, int64_t S, int32_t H_q, int32_t H_kv, int32_t d) {
   LayerPlan p;
-  p.n_qkv = (int64_t)(H_q + 2 * H_kv) * d;
+  p.n_qkv = ((int64_t)H_q + 2 * (int64_t)H_kv) * d;
   p.qkv_bytes = round_up(B * S * p.n_qkv * 2, 256);
   p.attn_bytes = round_up(B * S * (int64_t)H_q * d * 2, 256);
   p.gemm_ws_bytes = kGemmWorkspace;

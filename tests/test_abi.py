@@ -61,6 +61,16 @@ def test_unsupported(kw):
     assert _call(**kw) == sqa.SQA_ERR_UNSUPPORTED
 
 
+def test_row_too_wide_is_unsupported():
+    # tiles are addressed with 32-bit offsets from a 64-bit base: rows of at
+    # most 2^22 elements
+    assert _call(S=1, H_q=65536, H_kv=65536) == sqa.SQA_ERR_UNSUPPORTED
+    assert _call(S=1, H_q=65536, H_kv=1) == sqa.SQA_ERR_UNSUPPORTED
+    assert _call_bwd(S=1, H_q=65536, H_kv=65536) == sqa.SQA_ERR_UNSUPPORTED
+    assert _call_dec(S_max=1, H_q=65536, H_kv=65536) == sqa.SQA_ERR_UNSUPPORTED
+    assert _call_layer(S=1, d_model=8, H_q=16384, H_kv=16384) == sqa.SQA_ERR_UNSUPPORTED
+
+
 def test_sequence_too_long_is_unsupported():
     far = 1 << 44   # buffers spaced wider than the 2^41-byte tensors
     assert _call(q=far, k=2 * far, v=3 * far, out=4 * far, S=(1 << 30) + 1) == sqa.SQA_ERR_UNSUPPORTED
