@@ -79,3 +79,31 @@ def test_decode_million_position_cache():
     st = parity.check(gpu_util.to_host_f64(out), ref, "bf16", "decode S_max=2^20")
     assert np.abs(lse.double().cpu().numpy() - ref_lse).max() <= LSE_MAX
     _say(f"  {st}")
+
+
+def test_forward_tensors_past_4_gib():
+    """q and out of 2^19 x 32 x 128 bf16 elements (4 GiB each, element
+    offsets up to 2^31): the rows at the far end need 64-bit addressing.
+    Inputs are a seeded 4096-row block repeated along the sequence (the
+    causal mask still makes every row's softmax different)."""
+    B, S, H_q, H_kv, d, blk = 1, 1 << 19, 32, 8, 128, 4096
+    _say(f"forward B={B} S={S} H={H_q}/{H_kv} d={d} causal, q = 4 GiB")
+    reps = S // blk
+    q = np.tile(inputs.normal(98, 0, (B, blk, H_q, d), "bf16", 0.5), (1, reps, 1, 1))
+    k = np.tile(inputs.normal(98, 1, (B, blk, H_kv, d), "bf16", 0.5), (1, reps, 1, 1))
+    v = np.tile(inputs.normal(98, 2, (B, blk, H_kv, d), "bf16", 0.5), (1, reps, 1, 1))
+    dq, dk, dv = (gpu_util.to_device(a) for a in (q, k, v))
+    o, lse = sqa.attn_fwd(dq, dk, dv, scale=1 / math.sqrt(d), causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    rows = np.array([0, 4095, 4096, (1 << 18) + 7, S - 33, S - 1])
+    idx = torch.from_numpy(rows).to(o.device)
+    got = gpu_util.to_host_f64(o[:, idx])
+    got_lse = lse[:, idx].double().cpu().numpy()
+    del o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    sc = float(np.float32(1 / math.sqrt(d)))
+    ref = oracle.attention(q, k, v, sc, causal=True, rows=rows)
+    ref_lse = oracle.lse(q, k, sc, causal=True, rows=rows)
+    st = parity.check(got, ref, "bf16", "q, out = 4 GiB")
+    assert np.abs(got_lse - ref_lse).max() <= LSE_MAX
+    _say(f"  {st}")
