@@ -107,3 +107,39 @@ def test_forward_tensors_past_4_gib():
     st = parity.check(got, ref, "bf16", "q, out = 4 GiB")
     assert np.abs(got_lse - ref_lse).max() <= LSE_MAX
     _say(f"  {st}")
+
+
+def test_backward_tensors_past_4_gib():
+    """The backward at the same 4 GiB shape: dq at rows across the sequence
+    against the oracle, and the two identities that hold at any size
+    (sum_j dk_j = 0 since every row of dS sums to zero; sum_j dv_j = the
+    summed dout of the group's query heads since every row of P sums to one)."""
+    from tests.test_gpu_backward import _check_grad, dq_allowance
+    B, S, H_q, H_kv, d, blk = 1, 1 << 19, 32, 8, 128, 4096
+    _say(f"backward B={B} S={S} H={H_q}/{H_kv} d={d} causal, q = 4 GiB")
+    reps = S // blk
+    q = np.tile(inputs.normal(99, 0, (B, blk, H_q, d), "bf16", 0.5), (1, reps, 1, 1))
+    k = np.tile(inputs.normal(99, 1, (B, blk, H_kv, d), "bf16", 0.5), (1, reps, 1, 1))
+    v = np.tile(inputs.normal(99, 2, (B, blk, H_kv, d), "bf16", 0.5), (1, reps, 1, 1))
+    g = np.tile(inputs.normal(99, 5, (B, blk, H_q, d), "bf16", 1.0), (1, reps, 1, 1))
+    scale = 1 / math.sqrt(d)
+    dq_, dk_, dv_, dg = (gpu_util.to_device(a) for a in (q, k, v, g))
+    o, lse = sqa.attn_fwd(dq_, dk_, dv_, scale=scale, causal=True, return_lse=True)
+    gq, gk, gv = sqa.attn_bwd(dq_, dk_, dv_, o, dg, lse, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    del o, lse, dq_, dk_, dv_
+    rows = np.array([0, 4095, 4096, (1 << 18) + 7, S - 33, S - 1])
+    got = gpu_util.to_host_f64(gq[:, torch.from_numpy(rows).to(gq.device)])
+    sc = float(np.float32(scale))
+    ref = oracle.attention_grad_dq_rows(q, k, v, g, sc, rows, causal=True)
+    st = _check_grad(got, ref, "bf16", "dq rows, 4 GiB", dq_allowance(q, k, v, g, sc, True, rows=rows))
+    _say(f"  dq rows {st}")
+    R = H_q // H_kv
+    dk_sum = gk.double().sum(dim=1)
+    dk_scale = gk.double().abs().sum(dim=1)
+    assert float((dk_sum.abs() / dk_scale.clamp_min(1e-30)).max()) < 2e-2, "sum_j dk_j != 0"
+    dv_sum = gv.double().sum(dim=1)
+    g_sum = dg.double().reshape(B, S, H_kv, R, d).sum(dim=(1, 3))
+    err = float((dv_sum - g_sum).norm() / g_sum.norm())
+    assert err < 2e-2, f"sum_j dv_j vs summed dout: {err}"
+    _say(f"  identities ok (dv rel {err:.2e})")
