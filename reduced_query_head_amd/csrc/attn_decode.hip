@@ -167,12 +167,12 @@ __global__ __launch_bounds__(kWavesDec * 64, 2) void attn_decode_split_bf16(Deco
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KS) : "memory");
 
     // S^T = K Q^T: 32 keys x 32 query heads
+    // V of the next block in flight first (its buffer held block t-1, whose
+    // reads completed in the previous step), then K of the block after it
+    if (t + 1 < n_blk) cp.issue(v_base + (int64_t)(r0 + kBlk) * kv_stride, kv_stride, k1 - r0 - kBlk, vnext, 0);
     f32x16 s = (f32x16){};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s, 0, 0, 0);
-
-    // V of the next block and K of the block after it in flight
-    if (t + 1 < n_blk) cp.issue(v_base + (int64_t)(r0 + kBlk) * kv_stride, kv_stride, k1 - r0 - kBlk, vnext, 0);
     load_k(kf, r0 + 2 * kBlk);
     // keys past the split end: s[r] holds key r0 + 8*(r/4) + 4*half + r%4
     if (r0 + kBlk > k1) {
