@@ -390,7 +390,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
     // the dV/dK products of half 0 between those of half 1 (one wave per SIMD
     // here, so the overlap has to come from this wave's own instruction order).
     constexpr int NH = QT / 32;
-    // row statistics of one half (lse2, delta), read just before its softmax
+    // row statistics of one half (-lse2/c, -delta), read just before its
+    // S/dP products, which start from them
     auto load_stats = [&](int qh, float (&l2)[16], float (&dl)[16]) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
