@@ -107,3 +107,35 @@ def test_random_decode(B, S, H_q, H_kv, d, causal, scale):
     if (~empty).any():
         parity.check(got[~empty], ref[~empty], "bf16", "random decode")
         assert np.abs(got_lse[~empty] - ref_lse[~empty]).max() <= LSE_MAX
+
+
+# Shapes whose grid takes the 8-wave / 128-key kernel (at least 512
+# workgroups of 8 query blocks), checked in full: ragged tails (S % 128 = 1,
+# 104, 55, 63, 127), odd group sizes, both masks.
+LARGE = [
+    (2, 4097, 16, 16, 64, False),
+    (1, 4200, 32, 8, 128, True),
+    (2, 3000, 48, 16, 64, True),
+    (4, 2111, 24, 8, 128, False),
+    (1, 8191, 16, 2, 128, True),
+]
+
+
+@pytest.mark.parametrize("B,S,H_q,H_kv,d,causal", LARGE)
+def test_large_grid_forward_full(B, S, H_q, H_kv, d, causal):
+    items = (H_q // H_kv) * ((S + 31) // 32)
+    assert B * H_kv * ((items + 7) // 8) >= 512, "shape does not reach the 8-wave kernel"
+    _say(f"fwd (8-wave) B={B} S={S} H={H_q}/{H_kv} d={d} causal={causal}")
+    seed = 15000 + S + 7 * H_q + d
+    q = inputs.normal(seed, 0, (B, S, H_q, d), "bf16", 0.5)
+    k = inputs.normal(seed, 1, (B, S, H_kv, d), "bf16", 0.5)
+    v = inputs.normal(seed, 2, (B, S, H_kv, d), "bf16", 0.5)
+    dq, dk, dv = (gpu_util.to_device(a) for a in (q, k, v))
+    scale = 1 / math.sqrt(d)
+    o, lse = sqa.attn_fwd(dq, dk, dv, scale=scale, causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    sc = float(np.float32(scale))
+    st = parity.check(gpu_util.to_host_f64(o), oracle.attention(q, k, v, sc, causal=causal), "bf16", "8-wave forward")
+    err = np.abs(lse.double().cpu().numpy() - oracle.lse(q, k, sc, causal=causal))
+    assert err.max() <= LSE_MAX, f"lse {err.max()}"
+    _say(f"  {st}")
