@@ -71,7 +71,8 @@ struct BwdParams {
   int n_groups;      // B * H_kv
   int n_items;       // dq: R * ceil(S / 32) per group
   int chunks;        // dq: workgroups per group
-  int key_blocks;    // dk/dv: workgroups per group
+  int key_blocks;    // dk/dv: key blocks (workgroups) per group
+  int kb_chunk;      // dk/dv: 0, or key blocks of one group that one XCD takes in a row
   float c;           // |scale| * log2(e)
   float scale;       // signed scale
   uint32_t q_sign;   // 0x8000 when scale < 0: q (dq kernel) or k (dk/dv kernel) negated on load, exact
@@ -301,8 +302,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
   const int col = lane & 31;
   const int S = p.S;
 
-  const int grp = blockIdx.x % p.n_groups;
-  const int kb = blockIdx.x / p.n_groups;  // low keys first: they see the most queries when causal
+  // workgroup -> (group, key block); low keys first, as they see the most
+  // queries when causal.  With kb_chunk set, workgroups dealt to one XCD
+  // (blockIdx mod 8 under round-robin dispatch) take kb_chunk consecutive
+  // key blocks of one group, so that the query tiles in flight on that XCD
+  // span 2 * kb_chunk tiles of a head and stay in its L2.  Chunks go to XCDs
+  // heaviest first, the order reversed every other round to balance the
+  // XCDs; workgroups past the last key block exit at once.
+  int grp, kb;
+  if (p.kb_chunk) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int round = slot / p.kb_chunk;
+    const int unit = round * 8 + ((round & 1) ? 7 - xcd : xcd);
+    grp = unit % p.n_groups;
+    kb = (unit / p.n_groups) * p.kb_chunk + slot % p.kb_chunk;
+    if (kb >= p.key_blocks) return;
+  } else {
+    grp = blockIdx.x % p.n_groups;
+    kb = blockIdx.x / p.n_groups;
+  }
   const int b = grp / p.H_kv;
   const int g = grp % p.H_kv;
   const int key_wg0 = kb * KEYS_WG;
@@ -622,6 +640,20 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32(const float* q, const float*
   }
 }
 
+// dk/dv grid: one workgroup per (group, key block), or, for sequences of at
+// least 64 key blocks, 32-block chunks dealt to the 8 XCDs (the grid padded
+// to whole rounds of 8 chunks).
+int64_t dkdv_layout(int64_t n_groups, int64_t key_blocks, int* kb_chunk) {
+  constexpr int kChunk = 32;
+  if (key_blocks < 2 * kChunk) {
+    *kb_chunk = 0;
+    return n_groups * key_blocks;
+  }
+  *kb_chunk = kChunk;
+  const int64_t units = n_groups * ((key_blocks + kChunk - 1) / kChunk);
+  return (units + 7) / 8 * 8 * kChunk;
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_bf16_t(const BwdArgs& a) {
   BwdParams p;
@@ -653,8 +685,8 @@ hipError_t launch_bwd_bf16_t(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_stats_bf16<D>), dim3((unsigned)((stat_threads + 255) / 256)), dim3(256), 0, st, p, a.B);
   hipLaunchKernelGGL((bwd_dq_bf16<D, CAUSAL>), dim3((unsigned)((int64_t)p.n_groups * p.chunks)), dim3(kWaves * 64), 0,
                      st, p);
-  hipLaunchKernelGGL((bwd_dkdv_bf16<D, CAUSAL>), dim3((unsigned)((int64_t)p.n_groups * p.key_blocks)),
-                     dim3(kWaves * 64), 0, st, p);
+  const int64_t dkdv_grid = dkdv_layout(p.n_groups, p.key_blocks, &p.kb_chunk);
+  hipLaunchKernelGGL((bwd_dkdv_bf16<D, CAUSAL>), dim3((unsigned)dkdv_grid), dim3(kWaves * 64), 0, st, p);
   return hipGetLastError();
 }
 
@@ -685,7 +717,8 @@ int64_t bwd_workspace_bytes(int64_t B, int64_t S, int32_t H_q) { return 2 * B * 
 int64_t bwd_grid_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv) {
   const int64_t items = (int64_t)(H_q / H_kv) * ((S + kRows32 - 1) / kRows32);
   const int64_t a = B * H_kv * ((items + kWaves - 1) / kWaves);
-  const int64_t b = B * H_kv * ((S + kWaves * kRows32 - 1) / (kWaves * kRows32));
+  int kb_chunk;
+  const int64_t b = dkdv_layout(B * H_kv, (S + kWaves * kRows32 - 1) / (kWaves * kRows32), &kb_chunk);
   const int64_t c = (B * H_q * pad64(S) * 8 + 255) / 256;
   return a > b ? (a > c ? a : c) : (b > c ? b : c);
 }

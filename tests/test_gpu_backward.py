@@ -131,7 +131,18 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("B,S,H_q,H_kv,d,causal", SMALL)
+# Sequences of 64 key blocks (128 keys each) or more, where the dK/dV grid
+# deals 32-block chunks of a group to the XCDs: partial last chunks (67, 65
+# and 65 blocks), one and three groups (idle padding workgroups), a group of
+# two query heads, both masks.
+CHUNKED = [
+    (1, 8492, 2, 1, 32, True),
+    (1, 8250, 3, 3, 32, True),
+    (1, 8200, 1, 1, 32, False),
+]
+
+
+@pytest.mark.parametrize("B,S,H_q,H_kv,d,causal", SMALL + CHUNKED)
 def test_backward_small_shapes(B, S, H_q, H_kv, d, causal):
     _say(f"bwd B={B} S={S} H={H_q}/{H_kv} d={d} causal={causal}")
     seed = 9000 + S * 7 + H_q + d
