@@ -71,8 +71,13 @@ struct Bf16Params {
   int64_t kv_stride;     // same for k and v (H_kv * D when dense)
 };
 
+// Waves per SIMD the register allocation must allow: 4 for the d = 64,
+// 8-wave, 64-key shape (two workgroups per CU), else 2.
+template <int D, int WAVES, int KEYS>
+constexpr int fwd_min_waves_per_simd() { return (D == 64 && WAVES == 8 && KEYS == 64) ? 4 : 2; }
+
 template <int D, bool CAUSAL, int WAVES, int KEYS>
-__global__ __launch_bounds__(WAVES * 64, 2) void attn_fwd_bf16(Bf16Params p) {
+__global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>())) void attn_fwd_bf16(Bf16Params p) {
   constexpr int KS = D / 16;      // MFMA k-steps over the head dimension
   constexpr int DB = D / 32;      // 32-row blocks of O^T
   constexpr int NB = KEYS / 32;  // 32-key blocks per tile
@@ -362,11 +367,22 @@ hipError_t launch_bf16_w(const LaunchArgs& a) {
 
 constexpr int kCUs = 256;
 
+// Workgroup shape per head dim, when the grid of 8-wave workgroups still
+// fills the chip (else 4 waves and 64-key tiles, twice the workgroups):
+// - d = 128: 8 waves, 128-key tiles; 231 VGPRs, so one workgroup per CU
+//   (2 waves per SIMD); taken from 512 workgroups on.
+// - d = 64: 8 waves, 64-key tiles, held to 128 VGPRs so that two workgroups
+//   share a CU (4 waves per SIMD); taken from 256 workgroups on.  Measured
+//   2-5 % faster than 128-key tiles at 2 waves per SIMD.
+// - d = 32: 8 waves, 128-key tiles (126 VGPRs, two workgroups per CU); taken
+//   from 512 workgroups on.  4-5 % faster than the 4-wave shape.
 template <int D, bool CAUSAL>
 hipError_t launch_bf16_t(const LaunchArgs& a) {
-  if constexpr (D >= 64) {
-    const int64_t items = (int64_t)(a.H_q / a.H_kv) * ((a.S + kRows - 1) / kRows);
-    const int64_t wgs8 = a.B * a.H_kv * ((items + 7) / 8);
+  const int64_t items = (int64_t)(a.H_q / a.H_kv) * ((a.S + kRows - 1) / kRows);
+  const int64_t wgs8 = a.B * a.H_kv * ((items + 7) / 8);
+  if constexpr (D == 64) {
+    if (wgs8 >= kCUs) return launch_bf16_w<D, CAUSAL, 8, 64>(a);
+  } else {
     if (wgs8 >= 2 * kCUs) return launch_bf16_w<D, CAUSAL, 8, 128>(a);
   }
   return launch_bf16_w<D, CAUSAL, 4, 64>(a);

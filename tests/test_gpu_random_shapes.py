@@ -109,22 +109,27 @@ def test_random_decode(B, S, H_q, H_kv, d, causal, scale):
         assert np.abs(got_lse[~empty] - ref_lse[~empty]).max() <= LSE_MAX
 
 
-# Shapes whose grid takes the 8-wave / 128-key kernel (at least 512
-# workgroups of 8 query blocks), checked in full: ragged tails (S % 128 = 1,
-# 104, 55, 63, 127), odd group sizes, both masks.
+# Shapes whose grid takes the 8-wave kernel of their head dim (at least 512
+# workgroups of 8 query blocks at d = 128 and 32, 256 at d = 64), checked in
+# full: ragged tails (S mod 128 = 1, 4, 55, 56, 63, 104, 127), odd group
+# sizes, both masks, each head dim.
 LARGE = [
     (2, 4097, 16, 16, 64, False),
     (1, 4200, 32, 8, 128, True),
     (2, 3000, 48, 16, 64, True),
     (4, 2111, 24, 8, 128, False),
     (1, 8191, 16, 2, 128, True),
+    (2, 4100, 12, 4, 64, True),
+    (2, 4097, 16, 16, 32, False),
+    (2, 3000, 24, 8, 32, True),
 ]
 
 
 @pytest.mark.parametrize("B,S,H_q,H_kv,d,causal", LARGE)
 def test_large_grid_forward_full(B, S, H_q, H_kv, d, causal):
     items = (H_q // H_kv) * ((S + 31) // 32)
-    assert B * H_kv * ((items + 7) // 8) >= 512, "shape does not reach the 8-wave kernel"
+    need = 256 if d == 64 else 512
+    assert B * H_kv * ((items + 7) // 8) >= need, "shape does not reach the 8-wave kernel"
     _say(f"fwd (8-wave) B={B} S={S} H={H_q}/{H_kv} d={d} causal={causal}")
     seed = 15000 + S + 7 * H_q + d
     q = inputs.normal(seed, 0, (B, S, H_q, d), "bf16", 0.5)
