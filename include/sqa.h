@@ -32,9 +32,12 @@
  * page's transpose, so no transpose is needed on either side.
  *
  * Ownership.  The caller allocates and owns every buffer (device memory).
- * The library keeps no state, allocates nothing, and only enqueues work on
- * `stream` (the null stream is allowed); the call returns before the work is
- * done.  It is safe to call from several host threads at once.
+ * The attention entry points keep no state, allocate nothing, and only
+ * enqueue kernels on `stream` (the null stream is allowed); the call returns
+ * before the work is done, and it can be captured into a HIP graph.  The
+ * layer entry point also keeps a GEMM library handle per device (see
+ * sqa_layer_fwd).  All entry points are safe to call from several host
+ * threads at once.
  */
 #ifndef SQA_H
 #define SQA_H
