@@ -373,9 +373,9 @@ constexpr int kCUs = 256;
 //   (2 waves per SIMD); taken from 512 workgroups on.
 // - d = 64: 8 waves, 64-key tiles, held to 128 VGPRs so that two workgroups
 //   share a CU (4 waves per SIMD); taken from 256 workgroups on.  Measured
-//   2-5 % faster than 128-key tiles at 2 waves per SIMD.
+//   1.5-7 % faster than 128-key tiles at 2 waves per SIMD.
 // - d = 32: 8 waves, 128-key tiles (126 VGPRs, two workgroups per CU); taken
-//   from 512 workgroups on.  4-5 % faster than the 4-wave shape.
+//   from 512 workgroups on.  2-5 % faster than the 4-wave shape.
 template <int D, bool CAUSAL>
 hipError_t launch_bf16_t(const LaunchArgs& a) {
   const int64_t items = (int64_t)(a.H_q / a.H_kv) * ((a.S + kRows - 1) / kRows);
