@@ -19,17 +19,17 @@
 //    along MFMA M (S^T = K Q^T, dP^T = V dO^T) each lane owns one query, so
 //    D_i and lse_i are per-lane scalars; dQ^T += K^T dS^T reads K^T with
 //    transposing LDS reads.
-//  * bwd_dkdv: one wave per 32 keys of one K/V head (one wave per SIMD),
-//    its K and V rows staged once in LDS; query tiles of 64 rows (Q, dO and
-//    their statistics) of all R query heads of the group stream through LDS.
-//    S = Q K^T and dP = dO V^T put keys on lanes, so dV^T += dO^T P and
-//    dK^T += Q^T dS take P and dS straight from the accumulators and dO^T,
-//    Q^T from transposing LDS reads.  The accumulators start at
-//    -lse_i*log2(e)/c and -D_i, so they end at s - lse2/c and dP - D:
-//    P = 2^(c acc) and dS = P acc' with no per-score subtraction.  The two
-//    32-query halves of a tile form a two-stage pipeline in the instruction
-//    stream (half 1's products between half 0's softmax instructions and so
-//    on), since no second wave on the SIMD can fill the gaps.
+//  * bwd_dkdv: two waves per 32 keys of one K/V head, one per 32-query half
+//    of each 64-row query tile (Q, dO and their statistics, for all R query
+//    heads of the group, streamed through LDS); the workgroup's K and V rows
+//    are staged once in LDS.  Each wave holds half the score state, so two
+//    waves share a SIMD, and the halves' partial sums are added in LDS at
+//    the end.  S = Q K^T and dP = dO V^T put keys on lanes, so
+//    dV^T += dO^T P and dK^T += Q^T dS take P and dS straight from the
+//    accumulators and dO^T, Q^T from transposing LDS reads.  The
+//    accumulators start at -lse_i*log2(e)/c and -D_i, so they end at
+//    s - lse2/c and dP - D: P = 2^(c acc) and dS = P acc' with no per-score
+//    subtraction.
 //
 // All matrix products are bf16 MFMA with fp32 accumulation; P and dS are
 // rounded to bf16 for the products that consume them.  The fp32 path is plain
@@ -277,27 +277,43 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: 4 waves per workgroup, 32 keys per wave (128 keys per workgroup).
+// dK, dV: 8 waves per workgroup and 128 keys.  Wave w takes keys (w % 4) * 32
+// ... +31 and query half w / 4 of every 64-row query tile, so each wave holds
+// the score and dP accumulators of 32 queries only and two waves share each
+// SIMD: the other wave's matrix products fill the gaps of this one's
+// softmax.  The two halves' partial dK, dV are added through LDS at the end,
+// in a fixed order.
 // Copies of one query tile: Q rows and dO rows of head h (TileCopy), plus
 // the 256-byte runs of lse2 and delta, one copy each from its own 64-bit base
 // (lanes 0-15 carry the run; the others repeat it into unused LDS).
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
-  constexpr int WAVES = kWaves, QT = kTile;
+template <int D, bool CAUSAL, int MIN_WAVES_PER_SIMD>
+__global__ __launch_bounds__(512, MIN_WAVES_PER_SIMD) void bwd_dkdv_bf16(BwdParams p) {
+  constexpr int WAVES = 2 * kWaves, QT = kTile;
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int TILE = QT * D;
-  constexpr int KEYS_WG = WAVES * kRows32;
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_q0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_q1[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_g0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_g1[TILE];
-  __shared__ __attribute__((aligned(1024))) float lds_s0[512];  // [0,64) lse2, [256,320) delta
-  __shared__ __attribute__((aligned(1024))) float lds_s1[512];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_kk[KEYS_WG * D];   // this workgroup's K rows
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_vv[KEYS_WG * D];   // and V rows
+  constexpr int KEYS_WG = kWaves * kRows32;
+  // waves that copy the query tiles: all 8, or 4 when a tile is only 4
+  // wave-wide copies (d = 32)
+  constexpr int CW = (QT * D / 8 / 64) >= WAVES ? WAVES : kWaves;
+  // one LDS block with the four Q / dO tile buffers first, so that every
+  // read of them is one per-lane offset plus an immediate below 64 KiB (with
+  // separate arrays the compiler kept an address per buffer and spilled)
+  constexpr int TB = TILE * 2;          // bytes per tile buffer
+  constexpr int KVB = KEYS_WG * D * 2;  // bytes of the workgroup's K (or V) rows
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_all[4 * TB + 2 * KVB + 2 * 2048];
+  uint16_t* const lds_q0 = (uint16_t*)(lds_all + 0 * TB);
+  uint16_t* const lds_q1 = (uint16_t*)(lds_all + 1 * TB);
+  uint16_t* const lds_g0 = (uint16_t*)(lds_all + 2 * TB);
+  uint16_t* const lds_g1 = (uint16_t*)(lds_all + 3 * TB);
+  uint16_t* const lds_kk = (uint16_t*)(lds_all + 4 * TB);
+  uint16_t* const lds_vv = (uint16_t*)(lds_all + 4 * TB + KVB);
+  float* const lds_s0 = (float*)(lds_all + 4 * TB + 2 * KVB);          // [0,64) lse2, [256,320) delta
+  float* const lds_s1 = (float*)(lds_all + 4 * TB + 2 * KVB + 2048);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kw = wave % kWaves;  // key block of this wave
+  const int qh = wave / kWaves;  // query half of each tile
   const int half = lane >> 5;
   const int col = lane & 31;
   const int S = p.S;
@@ -324,7 +340,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
   const int b = grp / p.H_kv;
   const int g = grp % p.H_kv;
   const int key_wg0 = kb * KEYS_WG;
-  const int key0 = key_wg0 + wave * kRows32;
+  const int key0 = key_wg0 + kw * kRows32;
   const int my_key = key0 + col;
 
   // query tiles: R heads x tiles from the first one that can see this block
@@ -333,8 +349,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
   const int U = p.R * qt_count;
 
   const int64_t q_stride = (int64_t)p.H_q * D;
-  TileCopy<D, WAVES, QT> cp;
-  cp.init(q_stride, wave, lane);
+  TileCopy<D, CW, QT> cp;
+  if (wave < CW) cp.init(q_stride, wave, lane);
   // statistics of a tile: two 256-byte runs (lse2, delta) at 64-bit bases;
   // lanes 16-63 repeat lanes 0-15 into the unused rest of each 1 KiB half
   const uint32_t stat_lane = (uint32_t)(lane & 15) * 16u;
@@ -344,8 +360,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
     const int qt = qt_first + u % qt_count;
     const int h = g * p.R + hl;
     const int64_t base = (((int64_t)b * S + qt * QT) * p.H_q + h) * D;
-    cp.issue(p.q + base, q_stride, S - qt * QT, qd, wave);
-    cp.issue(p.dout + base, q_stride, S - qt * QT, gd, wave);
+    if (wave < CW) {
+      cp.issue(p.q + base, q_stride, S - qt * QT, qd, wave);
+      cp.issue(p.dout + base, q_stride, S - qt * QT, gd, wave);
+    }
     if (wave == 0) {
       const int64_t srow = ((int64_t)b * p.H_q + h) * p.S_pad + qt * QT;
       dma16(p.ws_lse2 + srow, stat_lane, lds_addr(sd));
@@ -353,17 +371,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
     }
   };
 
-  // K^T and V^T as B operands: lane holds key my_key, dims ks*16 + half*8 ...
-  // A negative scale is folded into k here (q streams through LDS unchanged),
-  // so that c * s = scale * log2(e) * <q, k> with c = |scale| * log2(e).
-  // K and V rows of this wave's keys go to LDS once (the K sign flipped for
-  // a negative scale); the products read them back as B operands: lane holds
-  // key my_key, dims ks*16 + half*8 ...
-  {
+  // K and V rows of the workgroup's keys go to LDS once (K's sign flipped
+  // for a negative scale, so that c * s = scale * log2(e) * <q, k> with
+  // c = |scale| * log2(e)); the half-0 waves write them, both halves read
+  // them as B operands (lane holds key my_key, dims ks*16 + half*8 ...)
+  // after the first tile's barrier.
+  if (qh == 0) {
     const int krow = min(my_key, S - 1);
     const int64_t off = (((int64_t)b * S + krow) * p.H_kv + g) * D + half * 8;
     const uint32_t sgn = p.q_sign * 0x10001u;
-    const int row = wave * kRows32 + col;
+    const int row = kw * kRows32 + col;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 raw = *(const u32x4*)(p.k + off + ks * 16);
@@ -373,21 +390,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
           *(const u32x4*)(p.v + off + ks * 16);
     }
   }
-  int b_off[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) b_off[ks] = tile_off<D>(wave * kRows32 + col, ks * 16 + half * 8);
   if (U > 0) issue_tile(0, (SQA_LDS uint16_t*)lds_q0, (SQA_LDS uint16_t*)lds_g0, (SQA_LDS float*)lds_s0);
 
-  int a_off[KS];  // Q / dO rows as the A operand: row col of the 32-row half
+  // row col of a 32-row block (a Q / dO half, or this wave's K / V rows):
+  // the swizzle depends on the low 4 row bits only, so one offset per k-step
+  // serves every block; the blocks' bases are wave-uniform
+  int c_off[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) a_off[ks] = tile_off<D>(col, ks * 16 + half * 8);
-  int t_off[DB][2];  // transposing reads of the Q / dO tile
+  for (int ks = 0; ks < KS; ++ks) c_off[ks] = tile_off<D>(col, ks * 16 + half * 8);
+  const SQA_LDS uint16_t* kk_w = (const SQA_LDS uint16_t*)lds_kk + kw * kRows32 * D;
+  const SQA_LDS uint16_t* vv_w = (const SQA_LDS uint16_t*)lds_vv + kw * kRows32 * D;
+  const int qh_base = qh * 32 * D;
+  // transposing reads of the Q / dO half: offsets of head-dim block 0; block
+  // db is the same offset with bit 5 replaced by db's bits (the swizzle
+  // leaves chunk bits 2-3 of these columns to db)
+  int t_off0[2];
   {
     const int grp16 = lane >> 4, i16 = lane & 15, e = i16 >> 2, c4 = i16 & 3;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) t_off[db][j] = tile_off<D>(4 * half + 8 * j + e, db * 32 + (grp16 & 1) * 16 + 4 * c4);
+    for (int j = 0; j < 2; ++j) t_off0[j] = tile_off<D>(4 * half + 8 * j + e, (grp16 & 1) * 16 + 4 * c4);
   }
 
   f32x16 dk[DB], dv[DB];
@@ -401,122 +422,70 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
     __syncthreads();
     if (u + 1 < U) issue_tile(u + 1, qn, gn, sn);
     const int qt = qt_first + u % qt_count;
-    const int q0 = qt * QT;
-    if (CAUSAL ? q0 + QT - 1 < key0 : q0 >= S) return;  // tile before this wave's keys / past the end
-    // Both 32-query halves of the tile, as a two-stage pipeline: the S/dP
-    // products of half 1 issue between the softmax instructions of half 0, and
-    // the dV/dK products of half 0 between those of half 1 (one wave per SIMD
-    // here, so the overlap has to come from this wave's own instruction order).
-    constexpr int NH = QT / 32;
-    // row statistics of one half (-lse2/c, -delta), read just before its
-    // S/dP products, which start from them
-    auto load_stats = [&](int qh, float (&l2)[16], float (&dl)[16]) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 a = *(const SQA_LDS f32x4*)(st_l + qh * 32 + 8 * j + 4 * half);
-        const f32x4 d4 = *(const SQA_LDS f32x4*)(st_l + 256 + qh * 32 + 8 * j + 4 * half);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          l2[4 * j + e] = a[e];
-          dl[4 * j + e] = d4[e];
-        }
-      }
-    };
+    const int qbase = qt * QT + qh * 32;
+    // this half before the wave's keys (causal) or past the end
+    if (CAUSAL ? qbase + 31 < key0 : qbase >= S) return;
     // S - lse2/c = Q K^T + (-lse2/c) and dP - D = dO V^T + (-D): the row
     // statistics (stored negated, lse2 divided by c) start the accumulators
     // (queries along M, this lane's key along N)
-    f32x16 s[NH], dp[NH];
+    f32x16 s, dp;
 #pragma unroll
-    for (int qh = 0; qh < NH; ++qh) {
-      float l2[16], dl[16];
-      load_stats(qh, l2, dl);
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 a = *(const SQA_LDS f32x4*)(st_l + qh * 32 + 8 * j + 4 * half);
+      const f32x4 d4 = *(const SQA_LDS f32x4*)(st_l + 256 + qh * 32 + 8 * j + 4 * half);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[qh][r] = l2[r];
-        dp[qh][r] = dl[r];
+      for (int e = 0; e < 4; ++e) {
+        s[4 * j + e] = a[e];
+        dp[4 * j + e] = d4[e];
       }
+    }
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a = *(const SQA_LDS bf16x8*)(qt_l + qh * 32 * D + a_off[ks]);
-        const bf16x8 kb = *(const SQA_LDS bf16x8*)((const SQA_LDS uint16_t*)lds_kk + b_off[ks]);
-        s[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kb, s[qh], 0, 0, 0);
-        const bf16x8 ga = *(const SQA_LDS bf16x8*)(gt_l + qh * 32 * D + a_off[ks]);
-        const bf16x8 vb = *(const SQA_LDS bf16x8*)((const SQA_LDS uint16_t*)lds_vv + b_off[ks]);
-        dp[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vb, dp[qh], 0, 0, 0);
-      }
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a = *(const SQA_LDS bf16x8*)(qt_l + qh_base + c_off[ks]);
+      const bf16x8 kb8 = *(const SQA_LDS bf16x8*)(kk_w + c_off[ks]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kb8, s, 0, 0, 0);
+      const bf16x8 ga = *(const SQA_LDS bf16x8*)(gt_l + qh_base + c_off[ks]);
+      const bf16x8 vb = *(const SQA_LDS bf16x8*)(vv_w + c_off[ks]);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vb, dp, 0, 0, 0);
+    }
+    // the accumulators of rows past S start at -inf (P = 0); only the
+    // causal mask is explicit, in a pass of its own (a branch, not selects)
+    const bool need_mask = CAUSAL && qbase < key0 + 31;
+    if (__builtin_expect(need_mask, 0)) {
+      asm volatile("" ::: "memory");
+      const int qlo = qbase + 4 * half;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (my_key > qlo + 8 * (r >> 2) + (r & 3)) s[r] = -__builtin_inff();
     }
     // P and dS = P (dP - D), rounded to bf16; query of register r:
     // qbase + 8*(r/4) + 4*half + r%4
-    bf16x8 pk[NH][2], dsk[NH][2];
+    bf16x8 pk[2], dsk[2];
 #pragma unroll
-    for (int qh = 0; qh < NH; ++qh) {
-      const int qbase = q0 + qh * 32;
-      // the accumulators of rows past S start at -inf (P = 0); only the causal mask is explicit
-      const bool need_mask = CAUSAL && qbase < key0 + 31;
-      if (__builtin_expect(need_mask, 0)) {
-        asm volatile("" ::: "memory");  // keeps this pass a branch
-        const int qlo = qbase + 4 * half;
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (my_key > qlo + 8 * (r >> 2) + (r & 3)) s[qh][r] = -__builtin_inff();
+      for (int e = 0; e < 8; ++e) {
+        const int r = st * 8 + e;
+        const float pv = __builtin_amdgcn_exp2f(s[r] * c);
+        pk[st][e] = (__bf16)pv;
+        dsk[st][e] = (__bf16)(pv * dp[r]);
       }
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = st * 8 + e;
-          const float pv = __builtin_amdgcn_exp2f(s[qh][r] * c);
-          pk[qh][st][e] = (__bf16)pv;
-          dsk[qh][st][e] = (__bf16)(pv * dp[qh][r]);
-        }
-    }
     // dV^T += dO^T P and dK^T += Q^T dS (16 queries per MFMA step)
 #pragma unroll
-    for (int qh = 0; qh < NH; ++qh)
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int ro = (qh * 32 + st * 16) * D;
-          const bf16x4 glo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SQA_LDS bf16x4*)(gt_l + ro + t_off[db][0]));
-          const bf16x4 ghi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SQA_LDS bf16x4*)(gt_l + ro + t_off[db][1]));
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                           pk[qh][st], dv[db], 0, 0, 0);
-          const bf16x4 qlo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SQA_LDS bf16x4*)(qt_l + ro + t_off[db][0]));
-          const bf16x4 qhi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SQA_LDS bf16x4*)(qt_l + ro + t_off[db][1]));
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(qlo4, qhi4, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                           dsk[qh][st], dk[db], 0, 0, 0);
-        }
-    // instruction order: half-0 stats and S/dP reads; half-0 S/dP; half-1 S/dP
-    // with half-0 softmax; half-0 dV/dK with half-1 softmax; half-1 dV/dK
-    static_assert(NH == 2, "the schedule below is written for two query halves");
-    // both halves' row statistics (8 reads each) and the first operands up
-    // front when non-causal; the causal kernel measured faster taking half
-    // 1's statistics in the reads that follow
-    __builtin_amdgcn_sched_group_barrier(0x100, CAUSAL ? 8 + 8 : 8 + 8 + 8, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * KS - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4 * DB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4 * DB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
+      for (int db = 0; db < DB; ++db) {
+        const int ro = qh_base + st * 16 * D;
+        const int t0 = t_off0[0] ^ (db << 5), t1 = t_off0[1] ^ (db << 5);
+        const bf16x4 glo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SQA_LDS bf16x4*)(gt_l + ro + t0));
+        const bf16x4 ghi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SQA_LDS bf16x4*)(gt_l + ro + t1));
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                         pk[st], dv[db], 0, 0, 0);
+        const bf16x4 qlo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SQA_LDS bf16x4*)(qt_l + ro + t0));
+        const bf16x4 qhi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((SQA_LDS bf16x4*)(qt_l + ro + t1));
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(qlo4, qhi4, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                         dsk[st], dk[db], 0, 0, 0);
+      }
   };
   for (int u = 0; u < U; u += 2) {
     step(u, (SQA_LDS uint16_t*)lds_q0, (SQA_LDS uint16_t*)lds_g0, (SQA_LDS float*)lds_s0, (SQA_LDS uint16_t*)lds_q1,
@@ -526,17 +495,52 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16(BwdParams p) {
            (SQA_LDS uint16_t*)lds_q0, (SQA_LDS uint16_t*)lds_g0, (SQA_LDS float*)lds_s0);
   }
 
-  if (my_key >= S) return;
+  // the half-1 waves hand their partial sums to the half-0 waves of the same
+  // keys through LDS (all tiles consumed, so the buffers are free): 16 KiB
+  // (d = 128) per array and wave, lane-contiguous 16-byte chunks
+  __syncthreads();
+  constexpr int RB = 64 * DB * 16;  // floats per wave and array
+  static_assert(RB * 4 <= TB && 2 * RB * 4 <= KVB, "reduction slots exceed the LDS buffers");
+  SQA_LDS float* red_k;
+  SQA_LDS float* red_v;
+  if (kw == 0) {
+    red_k = (SQA_LDS float*)lds_q0;
+    red_v = (SQA_LDS float*)lds_q1;
+  } else if (kw == 1) {
+    red_k = (SQA_LDS float*)lds_g0;
+    red_v = (SQA_LDS float*)lds_g1;
+  } else if (kw == 2) {
+    red_k = (SQA_LDS float*)lds_kk;
+    red_v = (SQA_LDS float*)lds_kk + RB;
+  } else {
+    red_k = (SQA_LDS float*)lds_vv;
+    red_v = (SQA_LDS float*)lds_vv + RB;
+  }
+  if (qh == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        *(SQA_LDS f32x4*)(red_k + ((db * 4 + j) * 64 + lane) * 4) =
+            (f32x4){dk[db][4 * j], dk[db][4 * j + 1], dk[db][4 * j + 2], dk[db][4 * j + 3]};
+        *(SQA_LDS f32x4*)(red_v + ((db * 4 + j) * 64 + lane) * 4) =
+            (f32x4){dv[db][4 * j], dv[db][4 * j + 1], dv[db][4 * j + 2], dv[db][4 * j + 3]};
+      }
+  }
+  __syncthreads();
+  if (qh == 1 || my_key >= S) return;
   const int64_t off = (((int64_t)b * S + my_key) * p.H_kv + g) * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      const f32x4 ok = *(const SQA_LDS f32x4*)(red_k + ((db * 4 + j) * 64 + lane) * 4);
+      const f32x4 ov = *(const SQA_LDS f32x4*)(red_v + ((db * 4 + j) * 64 + lane) * 4);
       bf16x4 wk, wv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        wk[e] = (__bf16)(dk[db][4 * j + e] * p.scale);
-        wv[e] = (__bf16)dv[db][4 * j + e];
+        wk[e] = (__bf16)((dk[db][4 * j + e] + ok[e]) * p.scale);
+        wv[e] = (__bf16)(dv[db][4 * j + e] + ov[e]);
       }
       *(bf16x4*)(p.dk + off + db * 32 + 8 * j + 4 * half) = wk;
       *(bf16x4*)(p.dv + off + db * 32 + 8 * j + 4 * half) = wv;
@@ -686,7 +690,17 @@ hipError_t launch_bwd_bf16_t(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_dq_bf16<D, CAUSAL>), dim3((unsigned)((int64_t)p.n_groups * p.chunks)), dim3(kWaves * 64), 0,
                      st, p);
   const int64_t dkdv_grid = dkdv_layout(p.n_groups, p.key_blocks, &p.kb_chunk);
-  hipLaunchKernelGGL((bwd_dkdv_bf16<D, CAUSAL>), dim3((unsigned)dkdv_grid), dim3(kWaves * 64), 0, st, p);
+  // d = 64 fits 128 VGPRs (a few values spilled; their reloads sit after
+  // the loop and, when causal, in the masked-tile pass), so two workgroups
+  // share a CU; that pays once the grid has 512 workgroups, while smaller
+  // grids run faster with more registers
+  if constexpr (D == 64) {
+    if ((int64_t)p.n_groups * p.key_blocks >= 512) {
+      hipLaunchKernelGGL((bwd_dkdv_bf16<D, CAUSAL, 4>), dim3((unsigned)dkdv_grid), dim3(2 * kWaves * 64), 0, st, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((bwd_dkdv_bf16<D, CAUSAL, 2>), dim3((unsigned)dkdv_grid), dim3(2 * kWaves * 64), 0, st, p);
   return hipGetLastError();
 }
 

@@ -140,9 +140,15 @@ CHUNKED = [
     (1, 8250, 3, 3, 32, True),
     (1, 8200, 1, 1, 32, False),
 ]
+# d = 64 grids of 512 or more dK/dV workgroups, which take the 4-waves-per-
+# SIMD build of that kernel: ragged S, both masks.
+WIDE = [
+    (4, 1000, 16, 16, 64, False),
+    (8, 1000, 8, 8, 64, True),
+]
 
 
-@pytest.mark.parametrize("B,S,H_q,H_kv,d,causal", SMALL + CHUNKED)
+@pytest.mark.parametrize("B,S,H_q,H_kv,d,causal", SMALL + CHUNKED + WIDE)
 def test_backward_small_shapes(B, S, H_q, H_kv, d, causal):
     _say(f"bwd B={B} S={S} H={H_q}/{H_kv} d={d} causal={causal}")
     seed = 9000 + S * 7 + H_q + d
