@@ -129,10 +129,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdParams p) {
   constexpr int WAVES = kWaves, KEYS = kTile;
   constexpr int KS = D / 16, DB = D / 32, NB = KEYS / 32, NT = KEYS / 16;
   constexpr int TILE = KEYS * D;
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_k0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_k1[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_v0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_v1[TILE];
+  // the four K/V tile buffers in one LDS block, so that each read is one
+  // per-lane offset plus an immediate (separate arrays cost an address
+  // register per buffer and spilled at d = 128)
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_all[4 * TILE];
+  uint16_t* const lds_k0 = lds_all;
+  uint16_t* const lds_k1 = lds_all + TILE;
+  uint16_t* const lds_v0 = lds_all + 2 * TILE;
+  uint16_t* const lds_v1 = lds_all + 3 * TILE;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
