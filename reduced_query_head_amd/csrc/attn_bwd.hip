@@ -240,6 +240,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdParams p) {
         for (int r = 0; r < 16; ++r)
           if (nb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[nb][r] = -__builtin_inff();
     }
+    // exponentials through the dQ MFMAs ahead of the SIMD's other wave
+    // (as in the forward): 2 % faster at d = 128, same results
+    __builtin_amdgcn_s_setprio(2);
     bf16x8 dsk[NT];
 #pragma unroll
     for (int st = 0; st < NT; ++st)
@@ -260,6 +263,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdParams p) {
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, dsk[st], acc[db], 0, 0, 0);
       }
     lds_mfma_pipeline_hint<NT * DB, 2, 4>();
+    __builtin_amdgcn_s_setprio(0);
   };
   for (int t = 0; t < n_tiles; t += 2) {
     step(t, (SQA_LDS uint16_t*)lds_k0, (SQA_LDS uint16_t*)lds_v0, (SQA_LDS uint16_t*)lds_k1, (SQA_LDS uint16_t*)lds_v1);
@@ -464,6 +468,10 @@ __global__ __launch_bounds__(512, MIN_WAVES_PER_SIMD) void bwd_dkdv_bf16(BwdPara
     }
     // P and dS = P (dP - D), rounded to bf16; query of register r:
     // qbase + 8*(r/4) + 4*half + r%4
+    // the 4-waves-per-SIMD build issues its exponentials and dV/dK MFMAs
+    // ahead of the SIMD's other waves (7-11 % faster there; no gain, or a
+    // loss, at 2 waves per SIMD)
+    if constexpr (MIN_WAVES_PER_SIMD == 4) __builtin_amdgcn_s_setprio(2);
     bf16x8 pk[2], dsk[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st)
@@ -490,6 +498,7 @@ __global__ __launch_bounds__(512, MIN_WAVES_PER_SIMD) void bwd_dkdv_bf16(BwdPara
         dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(qlo4, qhi4, 0, 1, 2, 3, 4, 5, 6, 7),
                                                          dsk[st], dk[db], 0, 0, 0);
       }
+    if constexpr (MIN_WAVES_PER_SIMD == 4) __builtin_amdgcn_s_setprio(0);
   };
   for (int u = 0; u < U; u += 2) {
     step(u, (SQA_LDS uint16_t*)lds_q0, (SQA_LDS uint16_t*)lds_g0, (SQA_LDS float*)lds_s0, (SQA_LDS uint16_t*)lds_q1,

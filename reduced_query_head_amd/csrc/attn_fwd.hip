@@ -232,6 +232,11 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
     }
+    // From the exponentials to the last P.V MFMA this wave issues ahead of
+    // the other wave on its SIMD (which is then in its K.Q^T or maximum
+    // phase): measured 1-2 % faster at d = 128 and 2-7 % at d = 64, with the
+    // same results.
+    __builtin_amdgcn_s_setprio(2);
     const float neg_m = -m_run;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -264,6 +269,7 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
       }
     }
     lds_mfma_pipeline_hint<NT * DB, 2, 4>();
+    __builtin_amdgcn_s_setprio(0);
     l_run += psum;
   };
   for (int t = 0; t < n_tiles; t += 2) {
