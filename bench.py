@@ -301,7 +301,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
+        print("bench.py: libsqa runs on one GPU only; --gpus must be 1 "
               "(sharding across GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
 

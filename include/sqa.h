@@ -54,7 +54,7 @@ typedef struct ihipStream_t* sqa_stream_t;
 typedef enum {
   SQA_OK = 0,
   SQA_ERR_INVALID_ARGUMENT = 1, /* a documented precondition does not hold */
-  SQA_ERR_UNSUPPORTED = 2,      /* valid arguments this build has no kernel for */
+  SQA_ERR_UNSUPPORTED = 2,      /* valid arguments the library has no kernel for */
   SQA_ERR_HIP = 3               /* the HIP runtime refused the launch */
 } sqa_status;
 
