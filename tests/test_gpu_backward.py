@@ -208,6 +208,27 @@ def test_backward_scale_values(scale):
             assert float(gpu_util.to_host_f64(gk).__abs__().max()) == 0.0
 
 
+@pytest.mark.parametrize("B,S,H_q,H_kv,d,causal", [(4, 1000, 16, 16, 64, True), (2, 640, 8, 2, 32, False)])
+def test_backward_negative_scale_other_builds(B, S, H_q, H_kv, d, causal):
+    """A negative scale (folded into K's sign when the dK/dV kernel stages its
+    rows) on the d = 64 4-waves-per-SIMD dK/dV build (512 workgroups) and on
+    the d = 32 build, whose query tiles are copied by 4 of its 8 waves."""
+    _say(f"bwd negative scale B={B} S={S} H={H_q}/{H_kv} d={d} causal={causal}")
+    scale = -0.6 / math.sqrt(d)
+    seed = 9500 + S + H_q + d
+    q = inputs.normal(seed, 0, (B, S, H_q, d), "bf16", 0.5)
+    k = inputs.normal(seed, 1, (B, S, H_kv, d), "bf16", 0.5)
+    v = inputs.normal(seed, 2, (B, S, H_kv, d), "bf16", 0.5)
+    dout = inputs.normal(seed, 5, (B, S, H_q, d), "bf16", 1.0)
+    gq, gk, gv = _run(q, k, v, dout, scale, causal)
+    sc = float(np.float32(scale))
+    rq, rk, rv = oracle.attention_grad(q, k, v, dout, sc, causal=causal)
+    allow = {"dq": dq_allowance(q, k, v, dout, sc, causal), "dk": dk_allowance(q, k, v, dout, sc, causal), "dv": None}
+    for name, got, ref in (("dq", gq, rq), ("dk", gk, rk), ("dv", gv, rv)):
+        st = _check_grad(gpu_util.to_host_f64(got), ref, "bf16", f"{name} scale={scale:.3g} d={d}", allow[name])
+        _say(f"  {name} {st}")
+
+
 @pytest.mark.parametrize("d", [32, 64, 128])
 def test_backward_f32(d):
     B, S, H_q, H_kv = 1, 100, 4, 2
