@@ -243,19 +243,19 @@ __global__ __launch_bounds__(kWavesDec * 64, 2) void attn_decode_split_bf16(Deco
 
 // One workgroup per (b, h, 32-dim chunk): merge the non-empty splits of that
 // head for 32 of its head dims.  The 256 threads form 32 split groups of 8
-// lanes, each lane holding 4 head dims (16-byte loads); a maximum pass over
-// the splits, a weighted-sum pass, then an LDS reduction over the groups.
+// lanes, each lane holding 4 head dims (16-byte loads).  One pass over the
+// splits, each group with its own running maximum, then an LDS reduction
+// over the groups (a separate maximum pass before the weighted sum made this
+// kernel 0.2-0.3 us, about 5 %, slower).
 template <int D>
 __global__ __launch_bounds__(256) void attn_decode_combine_bf16(DecodeParams p) {
   constexpr int DC = D / 32;            // dim chunks per head
   constexpr int LANES = 8;              // lanes per split group
   constexpr int SG = 256 / LANES;       // split groups
-  __shared__ float red_m[4];
+  __shared__ float red_mg[SG];
   __shared__ float red_l[SG];
   __shared__ f32x4 red_o[SG][LANES];
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
   const int grp = tid / LANES;
   const int dl = tid % LANES;
   const int64_t row = blockIdx.x / DC;      // b * H_q + h
@@ -272,33 +272,39 @@ __global__ __launch_bounds__(256) void attn_decode_combine_bf16(DecodeParams p) 
   const float* ml = p.part_ml + row * p.n_splits * 2;
   const float* po = p.part_o + row * p.n_splits * D + dc * 32;
 
-  float M = -__builtin_inff();
-  for (int s = tid; s < n_valid; s += 256) M = fmaxf(M, ml[2 * s]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (lane == 0) red_m[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-
+  // one pass: each split group keeps its own running maximum and rescales
+  // its sums when it grows; the groups are then combined with their maxima
+  float Mg = -__builtin_inff();
   float L = 0.f;
   f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
   for (int s = grp; s < n_valid; s += SG) {
     const float2 mls = *(const float2*)(ml + 2 * s);
-    const float w = __builtin_amdgcn_exp2f(mls.x - M);
-    L += w * mls.y;
-    acc += w * *(const f32x4*)(po + (int64_t)s * D + dl * 4);
+    const f32x4 o = *(const f32x4*)(po + (int64_t)s * D + dl * 4);
+    const float mn = fmaxf(Mg, mls.x);
+    const float a = __builtin_amdgcn_exp2f(Mg - mn);
+    const float w = __builtin_amdgcn_exp2f(mls.x - mn);
+    L = L * a + w * mls.y;
+    acc = acc * a + w * o;
+    Mg = mn;
   }
   red_o[grp][dl] = acc;
-  if (dl == 0) red_l[grp] = L;
+  if (dl == 0) {
+    red_l[grp] = L;
+    red_mg[grp] = Mg;
+  }
   __syncthreads();
   if (tid < LANES) {
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int g2 = 0; g2 < SG; ++g2) M = fmaxf(M, red_mg[g2]);
     float Lt = 0.f;
     f32x4 o = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int g2 = 0; g2 < SG; ++g2) {
-      Lt += red_l[g2];
-      o += red_o[g2][tid];
+      const float wg = __builtin_amdgcn_exp2f(red_mg[g2] - M);
+      Lt += wg * red_l[g2];
+      o += wg * red_o[g2][tid];
     }
     const float inv = 1.0f / Lt;
     bf16x4 w4;
