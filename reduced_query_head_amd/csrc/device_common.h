@@ -57,10 +57,12 @@ __device__ __forceinline__ float wave_pair_sum(float x) {
 // writes LDS at lds + 16*i.  Issued from inline asm so that the compiler's
 // wait-count bookkeeping does not treat every later LDS read as dependent on
 // it (the caller waits for these copies explicitly with vmcnt before the
-// barrier that publishes the tile).  No output registers; M0 is set here and
-// is not used by any compiler-generated code in these kernels.
+// barrier that publishes the tile).  No output registers.  The LDS address
+// goes in through an M0 operand constraint, so the compiler itself writes M0
+// and knows its value at every copy (a plain clobber of M0, a reserved
+// register, would not make it preserve its own uses).
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds) : "memory");
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
 
 // Wait until this wave's outstanding global -> LDS copies have landed.
