@@ -24,6 +24,38 @@ class SqaError(RuntimeError):
         self.status = status
 
 
+def _check_buffer(name, t, shape, dtype, device):
+    """A caller-supplied output or lse tensor: on the GPU next to the inputs,
+    contiguous, with exactly the expected shape and dtype (the C ABI sees only
+    the address, so a wrong buffer would be written out of bounds)."""
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a GPU tensor on {device}")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}; "
+                         f"got {t.dtype} {tuple(t.shape)}")
+
+
+def _workspace(t, need, device):
+    """A caller-supplied workspace (or a new one): a contiguous GPU tensor on
+    `device` of at least `need` bytes.  Returns it and its size in bytes."""
+    import torch
+
+    if t is None:
+        t = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    if not t.is_cuda or t.device != device or not t.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous GPU tensor on {device}")
+    nbytes = t.numel() * t.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace holds {nbytes} bytes; {need} needed")
+    return t, nbytes
+
+
+def _check_inputs(tensors, device):
+    for name, t in tensors:
+        if not t.is_cuda or t.device != device:
+            raise ValueError(f"{name} must be a GPU tensor on {device}")
+
+
 def load_library(path=None):
     """Load libsqa.so (build it first if it is absent) and declare its symbols."""
     global _lib
@@ -103,10 +135,11 @@ def attn_fwd(q, k, v, out=None, scale=None, causal=False, stream=None, return_ls
     if tuple(k.shape[:2]) != (B, S) or k.shape[3] != d or k.shape != v.shape:
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     H_kv = k.shape[2]
+    _check_inputs((("k", k), ("v", v)), q.device)
     if out is None:
         out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
-        raise ValueError("out must be a contiguous GPU tensor shaped and typed like q")
+    else:
+        _check_buffer("out", out, q.shape, q.dtype, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if stream is None:
@@ -115,8 +148,8 @@ def attn_fwd(q, k, v, out=None, scale=None, causal=False, stream=None, return_ls
     if return_lse or lse is not None:
         if lse is None:
             lse = torch.empty((B, S, H_q), dtype=torch.float32, device=q.device)
-        elif lse.shape != (B, S, H_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
-            raise ValueError("lse must be a contiguous float32 tensor of shape [B, S, H_q]")
+        else:
+            _check_buffer("lse", lse, (B, S, H_q), torch.float32, q.device)
         st = attn_fwd_lse_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, S,
                               H_q, H_kv, d, dtype, float(scale), causal, handle)
         if st != SQA_OK:
@@ -163,21 +196,25 @@ def attn_bwd(q, k, v, out, dout, lse, scale=None, causal=False, stream=None, dq=
     H_kv = k.shape[2]
     if out.shape != q.shape or dout.shape != q.shape or k.shape != v.shape or tuple(k.shape[:2]) != (B, S):
         raise ValueError("shape mismatch")
-    if lse.shape != (B, S, H_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor of shape [B, S, H_q]")
+    _check_inputs((("k", k), ("v", v), ("out", out), ("dout", dout)), q.device)
+    _check_buffer("lse", lse, (B, S, H_q), torch.float32, q.device)
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t is not None:
+            _check_buffer(name, t, like.shape, like.dtype, q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     ws_bytes = attn_bwd_workspace_size(B, S, H_q)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    if ws_bytes < 0:
+        raise ValueError("invalid sizes")
+    workspace, ws_have = _workspace(workspace, ws_bytes, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     st = attn_bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(), B, S, H_q,
+                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), ws_have, B, S, H_q,
                       H_kv, d, dtype, float(scale), causal, handle)
     if st != SQA_OK:
         raise SqaError(st, status_string(st))
@@ -220,22 +257,21 @@ def attn_decode(q, k_cache, v_cache, seqlens=None, out=None, scale=None, stream=
     S_max, H_kv = k_cache.shape[1], k_cache.shape[2]
     if k_cache.shape[0] != B or k_cache.shape[3] != d:
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k_cache.shape)}")
-    if seqlens is not None and (not seqlens.is_cuda or seqlens.dtype != torch.int32 or seqlens.shape != (B,)
-                                or not seqlens.is_contiguous()):
-        raise ValueError("seqlens must be a contiguous int32 GPU tensor of shape [B]")
+    _check_inputs((("k_cache", k_cache), ("v_cache", v_cache)), q.device)
+    if seqlens is not None:
+        _check_buffer("seqlens", seqlens, (B,), torch.int32, q.device)
     if out is None:
         out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
-        raise ValueError("out must be a contiguous GPU tensor shaped and typed like q")
+    else:
+        _check_buffer("out", out, q.shape, q.dtype, q.device)
     if return_lse and lse is None:
         lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
-    if lse is not None and (lse.shape != (B, H_q) or lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 tensor of shape [B, H_q]")
+    if lse is not None:
+        _check_buffer("lse", lse, (B, H_q), torch.float32, q.device)
     ws_bytes = attn_decode_workspace_size(B, S_max, H_q, H_kv, d)
     if ws_bytes < 0:
         raise ValueError("invalid sizes")
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    workspace, ws_have = _workspace(workspace, ws_bytes, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if stream is None:
@@ -243,8 +279,8 @@ def attn_decode(q, k_cache, v_cache, seqlens=None, out=None, scale=None, stream=
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     st = attn_decode_raw(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                          seqlens.data_ptr() if seqlens is not None else None, out.data_ptr(),
-                         lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
-                         workspace.numel() * workspace.element_size(), B, S_max, H_q, H_kv, d, dtype,
+                         lse.data_ptr() if lse is not None else None, workspace.data_ptr(), ws_have,
+                         B, S_max, H_q, H_kv, d, dtype,
                          float(scale), handle)
     if st != SQA_OK:
         raise SqaError(st, status_string(st))
@@ -283,22 +319,22 @@ def layer_fwd(x, w_qkv, w_o, H_q, H_kv, out=None, scale=None, causal=False, stre
     d = rows_qkv // (H_q + 2 * H_kv)
     if w_qkv.shape[1] != d_model or tuple(w_o.shape) != (d_model, H_q * d):
         raise ValueError(f"weight shapes {tuple(w_qkv.shape)} {tuple(w_o.shape)} do not match x {tuple(x.shape)}")
+    _check_inputs((("w_qkv", w_qkv), ("w_o", w_o)), x.device)
     if out is None:
         out = torch.empty_like(x)
-    elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous() or not out.is_cuda:
-        raise ValueError("out must be a contiguous GPU tensor shaped and typed like x")
+    else:
+        _check_buffer("out", out, x.shape, x.dtype, x.device)
     ws_bytes = layer_workspace_size(B, S, H_q, H_kv, d)
     if ws_bytes < 0:
         raise ValueError("invalid sizes")
-    if workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    workspace, ws_have = _workspace(workspace, ws_bytes, x.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     st = layer_fwd_raw(x.data_ptr(), w_qkv.data_ptr(), w_o.data_ptr(), out.data_ptr(), workspace.data_ptr(),
-                       workspace.numel() * workspace.element_size(), B, S, d_model, H_q, H_kv, d, float(scale),
+                       ws_have, B, S, d_model, H_q, H_kv, d, float(scale),
                        causal, handle)
     if st != SQA_OK:
         raise SqaError(st, status_string(st))
