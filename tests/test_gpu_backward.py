@@ -146,9 +146,19 @@ WIDE = [
     (4, 1000, 16, 16, 64, False),
     (8, 1000, 8, 8, 64, True),
 ]
+# The chunked dK/dV grid at the head sizes of the long workloads: d = 128
+# with a group of two query heads and a ragged last key block (65 blocks,
+# the last one 108 keys long), both masks; and d = 64 with 8 groups of 64
+# key blocks (512 workgroups, so the 4-waves-per-SIMD build runs chunked).
+# dq, dk and dv are compared element by element in full.
+CHUNKED_LARGE = [
+    (1, 8300, 2, 1, 128, True),
+    (1, 8300, 2, 1, 128, False),
+    (1, 8100, 8, 8, 64, True),
+]
 
 
-@pytest.mark.parametrize("B,S,H_q,H_kv,d,causal", SMALL + CHUNKED + WIDE)
+@pytest.mark.parametrize("B,S,H_q,H_kv,d,causal", SMALL + CHUNKED + WIDE + CHUNKED_LARGE)
 def test_backward_small_shapes(B, S, H_q, H_kv, d, causal):
     _say(f"bwd B={B} S={S} H={H_q}/{H_kv} d={d} causal={causal}")
     seed = 9000 + S * 7 + H_q + d
