@@ -537,35 +537,44 @@ def test_decode_bf16_inputs_decode_exactly():
 # full layer: projections around the attention
 
 
-def _torch_layer_module(x, w_qkv, w_o, H_q, H_kv, d, scale, causal):
-    """The GQA explainer's module structure in torch fp64 (CPU): separate q, k,
-    v linear maps, K/V expanded to the query heads with unsqueeze/expand/
-    reshape, SDPA on [B, H, T, d], output linear map."""
-    tx, tw, to = (torch.from_numpy(np.asarray(a, dtype=np.float64)) for a in (x, w_qkv, w_o))
-    B, T, _ = tx.shape
-    nq, nkv = H_q * d, H_kv * d
-    q = torch.nn.functional.linear(tx, tw[:nq]).view(B, T, H_q, d).transpose(1, 2)
-    k = torch.nn.functional.linear(tx, tw[nq:nq + nkv]).view(B, T, H_kv, d).transpose(1, 2)
-    v = torch.nn.functional.linear(tx, tw[nq + nkv:]).view(B, T, H_kv, d).transpose(1, 2)
+def _layer_per_head_fp64(x, w_qkv, w_o, H_q, H_kv, d, scale, causal):
+    """The layer written out head by head in numpy fp64, independently of the
+    oracle: query head h projects x with its own d rows of the q block, reads
+    the K/V projection of group g = h // (H_q / H_kv), weighs the visible
+    positions by exp(scale * score) normalised to sum 1, and the concatenated
+    head outputs go through the output projection."""
+    x = np.asarray(x, dtype=np.float64)
+    B, T, _ = x.shape
     R = H_q // H_kv
-    k = k.unsqueeze(2).expand(-1, -1, R, -1, -1).reshape(B, H_q, T, d)
-    v = v.unsqueeze(2).expand(-1, -1, R, -1, -1).reshape(B, H_q, T, d)
-    a = torch.nn.functional.scaled_dot_product_attention(q.contiguous(), k.contiguous(), v.contiguous(),
-                                                         is_causal=causal, scale=scale)
-    a = a.transpose(1, 2).contiguous().view(B, T, nq)
-    return torch.nn.functional.linear(a, to).numpy()
+    wq = w_qkv[:H_q * d]
+    wk = w_qkv[H_q * d:(H_q + H_kv) * d]
+    wv = w_qkv[(H_q + H_kv) * d:]
+    out = np.zeros((B, T, w_o.shape[0]))
+    for b in range(B):
+        for t in range(T):
+            heads = []
+            for h in range(H_q):
+                g = h // R
+                qh = wq[h * d:(h + 1) * d] @ x[b, t]
+                n = t + 1 if causal else T
+                keys = x[b, :n] @ wk[g * d:(g + 1) * d].T          # [n, d]
+                vals = x[b, :n] @ wv[g * d:(g + 1) * d].T
+                a = np.exp(scale * (keys @ qh))
+                heads.append((a / a.sum()) @ vals)
+            out[b, t] = w_o @ np.concatenate(heads)
+    return out
 
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("H_q,H_kv", [(4, 4), (8, 2), (2, 2), (4, 1)])
-def test_layer_matches_torch_module_fp64(H_q, H_kv, causal):
+def test_layer_matches_per_head_fp64(H_q, H_kv, causal):
     rng = np.random.default_rng(300 + H_q * 10 + H_kv)
     B, T, dm, d = 2, 19, 24, 8
     x = rng.standard_normal((B, T, dm))
     w_qkv = rng.standard_normal(((H_q + 2 * H_kv) * d, dm)) / math.sqrt(dm)
     w_o = rng.standard_normal((dm, H_q * d)) / math.sqrt(H_q * d)
     ours = oracle.layer(x, w_qkv, w_o, H_q, H_kv, d, 0.33, causal=causal)
-    ref = _torch_layer_module(x, w_qkv, w_o, H_q, H_kv, d, 0.33, causal)
+    ref = _layer_per_head_fp64(x, w_qkv, w_o, H_q, H_kv, d, 0.33, causal)
     np.testing.assert_allclose(ours, ref, rtol=1e-11, atol=1e-12)
 
 
