@@ -81,8 +81,8 @@ def time_variant(sqa, torch, w, variant, steps, warmup):
     flops = algorithmic_flops(w.B, w.S, v.H_q, w.d, w.causal)
     total_ms = ev[0].elapsed_time(ev[steps])
     res = dict(H_q=v.H_q, H_kv=v.H_kv, flops=flops, ms_per_step=total_ms / steps,
-               avg_launch_ms=sum(per_launch) / steps, min_launch_ms=min(per_launch),
-               max_launch_ms=max(per_launch), wall_s=wall)
+               avg_launch_ms=sum(per_launch) / steps, median_launch_ms=sorted(per_launch)[steps // 2],
+               min_launch_ms=min(per_launch), max_launch_ms=max(per_launch), wall_s=wall)
     res["tflops"] = flops / (res["ms_per_step"] * 1e-3) / 1e12
     res["tokens_per_s"] = w.B * w.S / (res["ms_per_step"] * 1e-3)
     del dq, dk, dv, out
@@ -244,6 +244,78 @@ def gemm_context(torch, n=8192, iters=10):
     return {"op": f"torch.matmul bf16 {n}x{n}x{n}, random N(0,1)", "tflops": round(2 * n ** 3 / ms / 1e9, 1)}
 
 
+def roofline_block(w, variant, res):
+    """Roofline position of one forward launch: algorithmic flops per launch
+    over the average HIP-event launch duration, against the dense bf16 MFMA
+    peak; HBM traffic from the committed counter summary of this workload and
+    variant when it was taken on the current kernel source (else None)."""
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    achieved = res["flops"] / (res["avg_launch_ms"] * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": traffic_from_profile(w.name, variant),
+            "kernel": f"attn_fwd_bf16 (d={w.d}, causal={int(w.causal)})" if w.dtype == "bf16"
+            else f"attn_fwd_f32 (d={w.d})",
+            "flops_per_launch": res["flops"], "avg_launch_ms": round(res["avg_launch_ms"], 4),
+            "median_launch_ms": round(res["median_launch_ms"], 4)}
+
+
+def entry(w, variant, res):
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    return {"H_q": res["H_q"], "H_kv": res["H_kv"], "ms_per_step": round(res["ms_per_step"], 4),
+            "tflops": round(res["tflops"], 1), "pct_peak": round(100 * res["tflops"] / peak, 2),
+            "tokens_per_s": round(res["tokens_per_s"], 1), "roofline": roofline_block(w, variant, res)}
+
+
+def time_sweep(sqa, torch, steps, warmup):
+    """The S = 4096, d = 64 head-configuration sweep: every variant at the
+    same shape, with the speedup over MHA and over GQA (both 16 query heads)
+    next to the ideal ratio of query-head counts."""
+    from inputs.configs import WORKLOADS
+    sw = WORKLOADS["sweep_s4096"]
+    rs = {v.name: time_variant(sqa, torch, sw, v.name, steps, warmup) for v in sw.variants}
+    out = {}
+    for name, r in rs.items():
+        e = entry(sw, name, r)
+        for ref in ("mha", "gqa"):
+            e[f"speedup_vs_{ref}"] = round(rs[ref]["ms_per_step"] / r["ms_per_step"], 3)
+            e[f"ideal_vs_{ref}"] = round(rs[ref]["H_q"] / r["H_q"], 3)
+        out[name] = e
+    return {"workload": sw.name, "B": sw.B, "S": sw.S, "d": sw.d, "causal": sw.causal, "steps": steps,
+            "variants": out}
+
+
+def host_info():
+    """CPU model and hardware thread counts of the host the oracle runs on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": usable, "cpu_count": os.cpu_count()}
+
+
+def oracle_full(w, variant, threads):
+    """The fp64 oracle on one whole workload variant (every query row)."""
+    import inputs.configs as cfg
+    import oracle
+
+    v = w.variant(variant)
+    q, k, vv, _ = cfg.make_inputs(w, variant)
+    t0 = time.perf_counter()
+    oracle.attention(q, k, vv, w.scale, causal=w.causal, n_threads=threads)
+    t = time.perf_counter() - t0
+    flops = algorithmic_flops(w.B, w.S, v.H_q, w.d, w.causal)
+    return {"seconds": round(t, 3), "tflops": round(flops / t / 1e12, 5), "flops": flops}
+
+
 def cpu_baseline(w, variant, budget_s):
     """The fp64 oracle, unchanged, on a bounded sample of query positions of
     the same workload (all batches and heads of each sampled position)."""
@@ -269,10 +341,118 @@ def cpu_baseline(w, variant, budget_s):
         done.append(rows.size)
         i += chunk
     n_rows = sum(done)
-    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_rows} of {w.S} query positions (seeded random, all {w.B} batch x {v.H_q} "
-                      f"heads each) of {w.name}/{variant}; {t_used:.1f} s of oracle time; "
-                      f"full run extrapolated: {algorithmic_flops(w.B, w.S, v.H_q, w.d, w.causal) / (flops / t_used):.0f} s"}
+    res = {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n_rows} of {w.S} query positions (seeded random, all {w.B} batch x {v.H_q} "
+                     f"heads each) of {w.name}/{variant}; {t_used:.1f} s of oracle time; "
+                     f"full run extrapolated: {algorithmic_flops(w.B, w.S, v.H_q, w.d, w.causal) / (flops / t_used):.0f} s",
+           "threads": threads, "extrapolated_full_s": round(algorithmic_flops(w.B, w.S, v.H_q, w.d, w.causal)
+                                                            / (flops / t_used), 1)}
+    res.update(host_info())
+    return res
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def summarize_trace(directory, kernel_re, skip, flops=None):
+    """Markdown summary of a rocprofv3 --kernel-trace CSV: per matching kernel,
+    the launch durations after the first `skip` launches (the warm-ups)."""
+    rows = [r for r in _csv_rows(directory, "kernel_trace.csv") if re.search(kernel_re, r["Kernel_Name"])]
+    by_name = {}
+    for r in rows:
+        by_name.setdefault(r["Kernel_Name"], []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    lines = ["| Kernel | launches | timed (after warm-ups) | mean ms | median ms | min ms | max ms |",
+             "|---|---|---|---|---|---|---|"]
+    stats = {}
+    for name, ts in by_name.items():
+        ts.sort()
+        d = sorted((e - b) / 1e6 for b, e in ts[skip:])
+        if not d:
+            continue
+        mean, med = sum(d) / len(d), d[len(d) // 2]
+        stats[name] = (mean, med)
+        lines.append(f"| {name} | {len(ts)} | {len(d)} | {mean:.4f} | {med:.4f} | {d[0]:.4f} | {d[-1]:.4f} |")
+    if flops:
+        lines.append("")
+        for name, (mean, med) in stats.items():
+            lines.append(f"{name}: {flops:.4e} flop per launch -> {flops / (mean * 1e-3) / 1e12:.1f} TFLOP/s on the "
+                         f"mean ({100 * flops / (mean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS:.2f} % of "
+                         f"{PEAK_BF16_TFLOPS} TFLOP/s), {flops / (med * 1e-3) / 1e12:.1f} TFLOP/s on the median "
+                         f"({100 * flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS:.2f} %)")
+    return "\n".join(lines)
+
+
+def summarize_counters(directories, kernel_re, skip):
+    """Markdown table of rocprofv3 --pmc results: per counter, the values of
+    the matching kernel's dispatches after the first `skip`, and the same
+    counters on the 1 GiB calibration copy of the same run, if present."""
+    table, copies = {}, {}
+    for directory in directories:
+        for r in _csv_rows(directory, "counter_collection.csv"):
+            key = (directory, int(r["Dispatch_Id"]))
+            dest = copies if "copyBuffer" in r["Kernel_Name"] else (
+                table if re.search(kernel_re, r["Kernel_Name"]) else None)
+            if dest is not None:
+                dest.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    per_counter, cal = {}, {}
+    for directory in directories:
+        ids = sorted(k for k in table if k[0] == directory)[skip:]
+        for key in ids:
+            for cname, val in table[key].items():
+                per_counter.setdefault(cname, []).append(val)
+        for key in sorted(k for k in copies if k[0] == directory):
+            for cname, val in copies[key].items():
+                cal.setdefault(cname, []).append(val)
+    return per_counter, cal
+
+
+def counters_markdown(per_counter, cal):
+    lines = ["| Counter | dispatches | mean per dispatch | values |", "|---|---|---|---|"]
+    for cname in sorted(per_counter):
+        vals = per_counter[cname]
+        lines.append(f"| {cname} | {len(vals)} | {sum(vals) / len(vals):.5e} | "
+                     + " / ".join(f"{x:.5e}" for x in vals) + " |")
+    if cal:
+        lines += ["", "Calibration copy (1 GiB read and written by a plain device copy in the same run):", "",
+                  "| Counter | mean per copy |", "|---|---|"]
+        for cname in sorted(cal):
+            lines.append(f"| {cname} | {sum(cal[cname]) / len(cal[cname]):.5e} |")
+    return "\n".join(lines)
+
+
+def traffic_summary(fetch_dir, write_dir, kernel_re, skip, w, variant):
+    """HBM bytes per launch from separate FETCH_SIZE and WRITE_SIZE runs,
+    each scaled by what the counter reads for the 1 GiB calibration copy of
+    the same run."""
+    pf, cf = summarize_counters([fetch_dir], kernel_re, skip)
+    pw, cw = summarize_counters([write_dir], kernel_re, skip)
+    n = 1 << 30
+    f_kib = sum(pf["FETCH_SIZE"]) / len(pf["FETCH_SIZE"])
+    w_kib = sum(pw["WRITE_SIZE"]) / len(pw["WRITE_SIZE"])
+    f_scale = n / 1024 / (sum(cf["FETCH_SIZE"]) / len(cf["FETCH_SIZE"]))
+    w_scale = n / 1024 / (sum(cw["WRITE_SIZE"]) / len(cw["WRITE_SIZE"]))
+    fb, wb = f_kib * 1024 * f_scale, w_kib * 1024 * w_scale
+    v = w.variant(variant)
+    elem = 2 if w.dtype == "bf16" else 4
+    alg_r = elem * w.B * w.S * w.d * (v.H_q + 2 * v.H_kv)
+    alg_w = elem * w.B * w.S * w.d * v.H_q
+    return "\n".join([
+        f"kernel_source_sha256_16: {kernel_source_hash()}",
+        f"hbm_bytes_per_launch: {fb + wb:.4e}",
+        "",
+        f"FETCH_SIZE: {f_kib:.1f} KiB per dispatch ({len(pf['FETCH_SIZE'])} dispatches), calibration factor "
+        f"{f_scale:.3f} -> {fb:.4e} bytes read per launch",
+        f"WRITE_SIZE: {w_kib:.1f} KiB per dispatch ({len(pw['WRITE_SIZE'])} dispatches), calibration factor "
+        f"{w_scale:.3f} -> {wb:.4e} bytes written per launch",
+        f"Algorithmic bytes per launch (Q, K, V read once, O written once): reads {alg_r:.4e}, writes {alg_w:.4e}; "
+        f"measured/algorithmic: reads {fb / alg_r:.2f}x, writes {wb / alg_w:.2f}x"])
 
 
 def main():
@@ -284,7 +464,11 @@ def main():
     ap.add_argument("--variant", default="sqa")
     ap.add_argument("--comparators", default="auto",
                     help="comma list of variants timed beside it, 'auto' = all others, 'none'")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time (0 = skip)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time (0 = skip)")
+    ap.add_argument("--cpu-full", choices=["auto", "none"], default="auto",
+                    help="also run the oracle whole on the tiny and S=4096 workloads (seconds)")
+    ap.add_argument("--sweep", choices=["auto", "none"], default="auto",
+                    help="time the S=4096 d=64 head-configuration sweep (MHA, GQA, SQA, xSQA)")
     ap.add_argument("--backward", choices=["auto", "none", "only"], default="auto",
                     help="time the backward too (auto: bf16 workloads), or only it")
     ap.add_argument("--long", choices=["auto", "none"], default="auto",
@@ -297,7 +481,28 @@ def main():
     ap.add_argument("--layer-workload", default="layer_s32k")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB (HBM counter calibration)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="run a plain 1 GiB device copy before the timed work (counter calibration in the same run)")
+    ap.add_argument("--summarize", choices=["trace", "counters", "traffic"],
+                    help="print a markdown summary of rocprofv3 CSV output instead of running (no GPU)")
+    ap.add_argument("--dirs", default="", help="comma list of rocprofv3 output folders for --summarize")
+    ap.add_argument("--kernel", default="attn_fwd_bf16", help="kernel-name regex for --summarize")
+    ap.add_argument("--skip", type=int, default=0, help="launches of the kernel to leave out (warm-ups)")
     args = ap.parse_args()
+
+    if args.summarize:
+        from inputs.configs import WORKLOADS
+        w = WORKLOADS[args.workload]
+        dirs = [d for d in args.dirs.split(",") if d]
+        if args.summarize == "trace":
+            v = w.variant(args.variant)
+            print(summarize_trace(dirs[0], args.kernel, args.skip,
+                                  algorithmic_flops(w.B, w.S, v.H_q, w.d, w.causal)))
+        elif args.summarize == "counters":
+            print(counters_markdown(*summarize_counters(dirs, args.kernel, args.skip)))
+        else:
+            print(traffic_summary(dirs[0], dirs[1], args.kernel, args.skip, w, args.variant))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -324,6 +529,15 @@ def main():
 
     w = WORKLOADS[args.workload]
     sqa.load_library()
+    if args.calibration_copy:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        torch.cuda.empty_cache()
     if args.layer == "only":
         print(json.dumps({"layer": time_layer(sqa, torch, args.layer_workload, args.steps, args.warmup)}),
               flush=True)
@@ -345,12 +559,8 @@ def main():
         comps[name]["sqa_speedup"] = comps[name]["ms_per_step"] / main_res["ms_per_step"]
         comps[name]["ideal_speedup"] = comps[name]["H_q"] / main_res["H_q"]
 
-    achieved = main_res["flops"] / (main_res["avg_launch_ms"] * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": traffic_from_profile(w.name, args.variant),
-                "kernel": f"attn_fwd_bf16<d={w.d},causal={int(w.causal)}>",
-                "flops_per_launch": main_res["flops"], "avg_launch_ms": round(main_res["avg_launch_ms"], 4)}
+    roofline = roofline_block(w, args.variant, main_res)
     longctx = None
     if args.long == "auto" and args.workload == "encoder_s32k":
         longctx = {}
@@ -358,17 +568,24 @@ def main():
             lw = WORKLOADS[wn]
             rs = {vv.name: time_variant(sqa, torch, lw, vv.name, 5, 2) for vv in lw.variants}
             first = lw.variants[0].name
-            longctx[wn] = {k: {"H_q": r["H_q"], "H_kv": r["H_kv"], "ms_per_step": round(r["ms_per_step"], 3),
-                               "tflops": round(r["tflops"], 1),
-                               "pct_peak": round(100 * r["tflops"] / PEAK_BF16_TFLOPS, 2),
-                               "tokens_per_s": round(r["tokens_per_s"], 1),
-                               "sqa_speedup": round(r["ms_per_step"] / rs[first]["ms_per_step"], 3) if k != first else 1.0}
-                           for k, r in rs.items()}
+            longctx[wn] = {}
+            for k, r in rs.items():
+                e = entry(lw, k, r)
+                e["sqa_speedup"] = round(r["ms_per_step"] / rs[first]["ms_per_step"], 3) if k != first else 1.0
+                e["ideal_speedup"] = round(r["H_q"] / rs[first]["H_q"], 3)
+                longctx[wn][k] = e
+    sweep = time_sweep(sqa, torch, 100, 10) if args.sweep == "auto" else None
     bwd = (time_backward(sqa, torch, w, args.variant, max(3, args.steps // 2), args.warmup)
            if args.backward == "auto" and w.dtype == "bf16" else None)
     dec = time_decode(sqa, torch, args.decode_workload, 20, 3) if args.decode == "auto" else None
     lay = time_layer(sqa, torch, args.layer_workload, 5, 2) if args.layer == "auto" else None
     cpu = cpu_baseline(w, args.variant, args.cpu_budget) if args.cpu_budget > 0 else None
+    if cpu is not None and args.cpu_full == "auto":
+        # the two workloads the oracle finishes whole in seconds
+        full = {"tiny_f32/gqa": oracle_full(WORKLOADS["tiny_f32"], "gqa", cpu["threads"])}
+        for vv in WORKLOADS["sweep_s4096"].variants:
+            full[f"sweep_s4096/{vv.name}"] = oracle_full(WORKLOADS["sweep_s4096"], vv.name, cpu["threads"])
+        cpu["full_runs"] = full
     gemm = gemm_context(torch) if args.cpu_budget > 0 else None
     v = w.variant(args.variant)
     line = {
@@ -395,6 +612,7 @@ def main():
                         for k, c in comps.items()},
         "roofline": roofline,
         "long_context": longctx,
+        "sweep": sweep,
         "backward": bwd,
         "decode": dec,
         "layer": lay,
