@@ -36,8 +36,10 @@
  * enqueue kernels on `stream` (the null stream is allowed); the call returns
  * before the work is done, and it can be captured into a HIP graph.  The
  * layer entry point also keeps a GEMM library handle per device (see
- * sqa_layer_fwd).  All entry points are safe to call from several host
- * threads at once.
+ * sqa_layer_fwd), and sqa_attn_decode_noalloc uses a fixed scratch array
+ * that the library holds on each GPU (see there).  All entry points are safe
+ * to call from several host threads at once (sqa_attn_decode_noalloc only
+ * when the calls' executions do not overlap on one GPU).
  */
 #ifndef SQA_H
 #define SQA_H
@@ -189,6 +191,35 @@ sqa_status sqa_attn_decode(const void* q, const void* k_cache, const void* v_cac
 
 /* Workspace bytes sqa_attn_decode needs; -1 for invalid sizes. */
 int64_t sqa_attn_decode_workspace_size(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d);
+
+/*
+ * Decode without a workspace, for callers that cannot allocate device memory
+ * (work captured into a HIP graph, tight serving loops, harnesses that forbid
+ * allocation).  Same computation, arguments and layout as sqa_attn_decode,
+ * minus the workspace: the split kernel's partial results go to a fixed
+ * scratch array of SQA_DECODE_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on until the process ends.  This call allocates nothing.  Its
+ * first call on a GPU looks up that GPU's copy of the array (a HIP symbol
+ * lookup, no allocation).
+ *
+ * Splits are lengthened, if needed, so that the partial results fit:
+ * B * H_q * n_splits * (d + 2) * 4 bytes <= SQA_DECODE_SCRATCH_BYTES.  The
+ * result can then differ from sqa_attn_decode's in rounding only (a
+ * different split of the same sum).  SQA_ERR_UNSUPPORTED when even one split
+ * per head does not fit: bf16 with B * H_q * (d + 2) * 4 >
+ * SQA_DECODE_SCRATCH_BYTES (more than 129055 sequence-heads at d = 128).
+ * fp32 inputs use no scratch.
+ *
+ * Every call on one GPU shares that GPU's array, and the array keeps the last
+ * call's contents: two calls whose execution overlaps on the same GPU (on
+ * different streams, or from different host threads without ordering) race
+ * on it and give undefined results.  Calls ordered on one stream are safe.
+ * Other errors as for sqa_attn_decode.
+ */
+#define SQA_DECODE_SCRATCH_BYTES ((int64_t)64 << 20)
+sqa_status sqa_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
+                                   void* out, float* lse, int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv,
+                                   int32_t d, sqa_dtype dtype, float scale, sqa_stream_t stream);
 
 /*
  * Full attention layer forward with decoupled head counts: the GQA

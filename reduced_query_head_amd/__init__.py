@@ -80,6 +80,9 @@ def load_library(path=None):
     lib.sqa_attn_decode.restype = ctypes.c_int
     lib.sqa_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, ctypes.c_int,
                                     ctypes.c_float, vp]
+    lib.sqa_attn_decode_noalloc.restype = ctypes.c_int
+    lib.sqa_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ctypes.c_int,
+                                            ctypes.c_float, vp]
     lib.sqa_attn_decode_workspace_size.restype = i64
     lib.sqa_attn_decode_workspace_size.argtypes = [i64, i64, i32, i32, i32]
     lib.sqa_layer_fwd.restype = ctypes.c_int
@@ -285,6 +288,13 @@ def attn_decode(q, k_cache, v_cache, seqlens=None, out=None, scale=None, stream=
     if st != SQA_OK:
         raise SqaError(st, status_string(st))
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def attn_decode_noalloc_raw(q, k_cache, v_cache, seqlens, out, lse, B, S_max, H_q, H_kv, d, dtype, scale, stream):
+    """Direct call of sqa_attn_decode_noalloc (no workspace: the library's
+    fixed per-GPU scratch holds the partial results); returns the status."""
+    return load_library().sqa_attn_decode_noalloc(q, k_cache, v_cache, seqlens, out, lse, B, S_max, H_q, H_kv, d,
+                                                  dtype, scale, stream)
 
 
 def layer_workspace_size(B, S, H_q, H_kv, d):

@@ -8,6 +8,8 @@
 
 #define SQA_API extern "C" __attribute__((visibility("default")))
 
+static_assert(sqa::kDecodeScratchBytes == SQA_DECODE_SCRATCH_BYTES, "scratch size differs from the header's");
+
 namespace {
 
 bool ranges_overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
@@ -194,15 +196,22 @@ SQA_API int64_t sqa_attn_decode_workspace_size(int64_t B, int64_t S_max, int32_t
   return sqa::decode_plan(B, S_max, H_q, H_kv, d).workspace_bytes;
 }
 
-SQA_API sqa_status sqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
-                                   void* out, float* lse, void* workspace, int64_t workspace_bytes, int64_t B,
-                                   int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d, sqa_dtype dtype,
-                                   float scale, sqa_stream_t stream) {
+namespace {
+
+// Checks shared by both decode entry points; fills *a on success.  With
+// no_alloc the partial results go to the library's fixed scratch instead of
+// a caller workspace, so `workspace` must be null and the split plan must fit
+// the scratch.
+sqa_status decode_checks(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
+                         void* out, float* lse, void* workspace, int64_t workspace_bytes, int64_t B,
+                         int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d, sqa_dtype dtype, float scale,
+                         sqa_stream_t stream, bool no_alloc, sqa::DecodeArgs* a) {
   if (B < 0 || S_max < 0 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0) return SQA_ERR_INVALID_ARGUMENT;
   if (dtype != SQA_BF16 && dtype != SQA_FP32) return SQA_ERR_INVALID_ARGUMENT;
   if (!isfinite(scale) || d < 1) return SQA_ERR_INVALID_ARGUMENT;
   if (B == 0) return SQA_OK;
-  if (!q || !out || !workspace || (S_max > 0 && (!k_cache || !v_cache))) return SQA_ERR_INVALID_ARGUMENT;
+  if (!q || !out || (!no_alloc && !workspace) || (S_max > 0 && (!k_cache || !v_cache)))
+    return SQA_ERR_INVALID_ARGUMENT;
   if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out | (uintptr_t)workspace) & 15u)
     return SQA_ERR_INVALID_ARGUMENT;
   if (((uintptr_t)lse | (uintptr_t)seqlens) & 3u) return SQA_ERR_INVALID_ARGUMENT;
@@ -213,12 +222,14 @@ SQA_API sqa_status sqa_attn_decode(const void* q, const void* k_cache, const voi
       !mul_ok(B, S_max, &cache_rows) || !mul_ok(cache_rows, (int64_t)H_kv * d, &kv_elems) ||
       !mul_ok(kv_elems, elem, &kv_bytes) || !mul_ok(B, (int64_t)H_q * 4, &lse_bytes))
     return SQA_ERR_INVALID_ARGUMENT;
-  const sqa::DecodePlan plan = sqa::decode_plan(B, S_max, H_q, H_kv, d);
-  if (workspace_bytes < plan.workspace_bytes) return SQA_ERR_INVALID_ARGUMENT;
+  const sqa::DecodePlan plan =
+      sqa::decode_plan(B, S_max, H_q, H_kv, d, no_alloc ? sqa::kDecodeScratchBytes : 0);
+  if (!no_alloc && workspace_bytes < plan.workspace_bytes) return SQA_ERR_INVALID_ARGUMENT;
+  const int64_t ws_bytes = no_alloc ? 0 : plan.workspace_bytes;
   const void* ins[4] = {q, k_cache, v_cache, seqlens};
   const int64_t in_bytes[4] = {q_bytes, kv_bytes, kv_bytes, seqlens ? B * 4 : 0};
-  const void* outs[3] = {out, lse, workspace};
-  const int64_t out_bytes[3] = {q_bytes, lse ? lse_bytes : 0, plan.workspace_bytes};
+  void* outs[3] = {out, lse, no_alloc ? nullptr : workspace};
+  const int64_t out_bytes[3] = {q_bytes, lse ? lse_bytes : 0, ws_bytes};
   for (int i = 0; i < 3; ++i) {
     if (!outs[i]) continue;
     for (int j = 0; j < 4; ++j)
@@ -231,28 +242,53 @@ SQA_API sqa_status sqa_attn_decode(const void* q, const void* k_cache, const voi
   // split grid (4 waves per workgroup), combine grid (d/32 workgroups per row), fp32 grid
   if ((plan.n_waves + 3) / 4 > INT32_MAX || B * H_q * (d / 32) > INT32_MAX || (B * H_q + 255) / 256 > INT32_MAX)
     return SQA_ERR_UNSUPPORTED;
+  // the fixed scratch holds at least one split of every head
+  if (no_alloc && dtype == SQA_BF16 && plan.workspace_bytes > sqa::kDecodeScratchBytes) return SQA_ERR_UNSUPPORTED;
 
-  sqa::DecodeArgs a;
-  a.q = q;
-  a.k = k_cache;
-  a.v = v_cache;
-  a.seqlens = seqlens;
-  a.out = out;
-  a.lse = lse;
-  a.workspace = workspace;
-  a.B = B;
-  a.S_max = S_max;
-  a.H_q = H_q;
-  a.H_kv = H_kv;
-  a.d = d;
-  a.dtype = dtype == SQA_BF16 ? 0 : 1;
+  a->q = q;
+  a->k = k_cache;
+  a->v = v_cache;
+  a->seqlens = seqlens;
+  a->out = out;
+  a->lse = lse;
+  a->workspace = no_alloc ? nullptr : workspace;
+  a->B = B;
+  a->S_max = S_max;
+  a->H_q = H_q;
+  a->H_kv = H_kv;
+  a->d = d;
+  a->dtype = dtype == SQA_BF16 ? 0 : 1;
   const float log2e = 1.4426950408889634f;
   const float mag = fabsf(scale);
-  a.c = mag > 0.f ? mag * log2e : 1e-30f;
-  if (!isfinite(a.c)) return SQA_ERR_INVALID_ARGUMENT;
-  a.negate_q = scale < 0.f;
-  a.stream = (void*)stream;
+  a->c = mag > 0.f ? mag * log2e : 1e-30f;
+  if (!isfinite(a->c)) return SQA_ERR_INVALID_ARGUMENT;
+  a->negate_q = scale < 0.f;
+  a->stream = (void*)stream;
+  return SQA_OK;
+}
+
+}  // namespace
+
+SQA_API sqa_status sqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
+                                   void* out, float* lse, void* workspace, int64_t workspace_bytes, int64_t B,
+                                   int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d, sqa_dtype dtype,
+                                   float scale, sqa_stream_t stream) {
+  sqa::DecodeArgs a;
+  const sqa_status st = decode_checks(q, k_cache, v_cache, seqlens, out, lse, workspace, workspace_bytes, B, S_max,
+                                      H_q, H_kv, d, dtype, scale, stream, false, &a);
+  if (st != SQA_OK || B == 0) return st;
   return sqa::launch_attn_decode(a) == hipSuccess ? SQA_OK : SQA_ERR_HIP;
+}
+
+SQA_API sqa_status sqa_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                           const int32_t* seqlens, void* out, float* lse, int64_t B, int64_t S_max,
+                                           int32_t H_q, int32_t H_kv, int32_t d, sqa_dtype dtype, float scale,
+                                           sqa_stream_t stream) {
+  sqa::DecodeArgs a;
+  const sqa_status st = decode_checks(q, k_cache, v_cache, seqlens, out, lse, nullptr, 0, B, S_max, H_q, H_kv, d,
+                                      dtype, scale, stream, true, &a);
+  if (st != SQA_OK || B == 0) return st;
+  return sqa::launch_attn_decode_noalloc(a) == hipSuccess ? SQA_OK : SQA_ERR_HIP;
 }
 
 SQA_API int64_t sqa_layer_workspace_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv, int32_t d) {

@@ -31,6 +31,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -418,7 +421,7 @@ hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& plan) {
 // cache 1-3 % faster).  Each split has at least 64 keys, and at least 16
 // keys per query head it serves, so the fp32 partial results written per
 // split stay within a few percent of the cache bytes it reads.
-DecodePlan decode_plan(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d) {
+DecodePlan decode_plan(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d, int64_t max_workspace) {
   DecodePlan pl;
   const int64_t R = H_q / H_kv;
   pl.head_blocks = (int)((R + 31) / 32);
@@ -433,6 +436,17 @@ DecodePlan decode_plan(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int3
   if (len < 64) len = 64;
   if (len < 16 * heads_per_wave) len = 16 * heads_per_wave;
   len = (len + kBlk - 1) / kBlk * kBlk;
+  // a workspace bound: at most max_workspace / (bytes per split of every
+  // head) splits, so each split covers at least S_max / that many keys
+  const int64_t per_split = B * H_q * (int64_t)(d + 2) * 4;
+  if (max_workspace > 0 && per_split > 0 && S_max > 0) {
+    const int64_t max_splits = max_workspace / per_split;
+    if (max_splits >= 1) {
+      int64_t fit = (S_max + max_splits - 1) / max_splits;
+      fit = (fit + kBlk - 1) / kBlk * kBlk;
+      if (fit > len) len = fit;
+    }
+  }
   pl.split_len = (int)len;
   pl.n_splits = (int)(S_max > 0 ? (S_max + len - 1) / len : 1);
   pl.part_o_bytes = B * H_q * (int64_t)pl.n_splits * d * 4;
@@ -441,7 +455,9 @@ DecodePlan decode_plan(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int3
   return pl;
 }
 
-hipError_t launch_attn_decode(const DecodeArgs& a) {
+namespace {
+
+hipError_t launch_decode_planned(const DecodeArgs& a, const DecodePlan& plan) {
   if (a.dtype == 1) {
     switch (a.d) {
       case 32: return launch_decode_f32_t<32>(a);
@@ -450,13 +466,67 @@ hipError_t launch_attn_decode(const DecodeArgs& a) {
     }
     return hipErrorInvalidValue;
   }
-  const DecodePlan plan = decode_plan(a.B, a.S_max, a.H_q, a.H_kv, a.d);
   switch (a.d) {
     case 32: return launch_decode_t<32>(a, plan);
     case 64: return launch_decode_t<64>(a, plan);
     case 128: return launch_decode_t<128>(a, plan);
   }
   return hipErrorInvalidValue;
+}
+
+// The fixed scratch of the allocation-free decode: the split kernel's
+// partial results, for callers that cannot allocate device memory.  The
+// runtime gives each GPU its own copy when it loads this code object; host
+// code reaches a GPU's copy only through the address hipGetSymbolAddress
+// returns with that GPU current (the array's name is a host-side stand-in).
+// Nothing in it has to start at zero: the split kernel writes every partial
+// result the combine kernel reads.
+__device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `device`'s scratch array, looked up once per device.
+hipError_t scratch_address(int device, void** ptr) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[device].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[device].load(std::memory_order_acquire);
+    if (!p) {
+      int current = -1;
+      hipError_t e = hipGetDevice(&current);
+      if (e != hipSuccess) return e;
+      if (current != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      const hipError_t e2 = current != device ? hipSetDevice(current) : hipSuccess;
+      if (e != hipSuccess) return e;
+      if (e2 != hipSuccess) return e2;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch_ptr[device].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_attn_decode(const DecodeArgs& a) {
+  return launch_decode_planned(a, decode_plan(a.B, a.S_max, a.H_q, a.H_kv, a.d));
+}
+
+hipError_t launch_attn_decode_noalloc(const DecodeArgs& a) {
+  const DecodePlan plan = decode_plan(a.B, a.S_max, a.H_q, a.H_kv, a.d, kDecodeScratchBytes);
+  if (a.dtype == 1) return launch_decode_planned(a, plan);   // the fp32 kernel uses no workspace
+  if (plan.workspace_bytes > kDecodeScratchBytes) return hipErrorInvalidValue;
+  DecodeArgs b = a;
+  int device = -1;
+  hipError_t e = a.stream ? hipStreamGetDevice((hipStream_t)a.stream, &device) : hipGetDevice(&device);
+  if (e != hipSuccess) return e;
+  if ((e = scratch_address(device, &b.workspace)) != hipSuccess) return e;
+  return launch_decode_planned(b, plan);
 }
 
 }  // namespace sqa

@@ -86,8 +86,17 @@ struct DecodePlan {
   int64_t workspace_bytes;
 };
 
-DecodePlan decode_plan(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d);
+// max_workspace > 0 lengthens the splits (fewer partial results) until the
+// workspace fits in that many bytes; workspace_bytes still exceeds it when
+// even one split per head does not fit.
+DecodePlan decode_plan(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d, int64_t max_workspace = 0);
 hipError_t launch_attn_decode(const DecodeArgs& a);
+
+// Bytes of the library's own fixed decode scratch (one array per GPU).
+constexpr int64_t kDecodeScratchBytes = (int64_t)64 << 20;
+// Decode with a.workspace ignored: the partial results go to that scratch
+// array of the stream's GPU; splits are planned to fit it.
+hipError_t launch_attn_decode_noalloc(const DecodeArgs& a);
 
 struct LayerArgs {
   const void* x;        // [B, S, d_model] bf16

@@ -218,3 +218,33 @@ def test_layer_unsupported(kw):
 
 def test_layer_empty():
     assert _call_layer(S=0, x=0, wqkv=0, wo=0, out=0, ws=0) == sqa.SQA_OK
+
+
+def _call_dec_noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE + G, v=FAKE + 2 * G, seqlens=FAKE + 3 * G, out=FAKE + 4 * G, lse=FAKE + 5 * G,
+             B=4, S_max=4096, H_q=32, H_kv=8, d=128, dtype=0, scale=0.088)
+    a.update(kw)
+    return sqa.attn_decode_noalloc_raw(a["q"], a["k"], a["v"], a["seqlens"], a["out"], a["lse"], a["B"],
+                                       a["S_max"], a["H_q"], a["H_kv"], a["d"], a["dtype"], a["scale"], 0)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(H_q=6, H_kv=4), dict(H_q=0), dict(B=-1), dict(S_max=-1), dict(dtype=5), dict(scale=float("nan")),
+    dict(q=0), dict(out=0), dict(k=0), dict(q=FAKE + 8), dict(lse=FAKE + 5 * G + 2),
+    dict(out=FAKE + 64),          # out overlaps q
+])
+def test_decode_noalloc_invalid_arguments(kw):
+    assert _call_dec_noalloc(**kw) == sqa.SQA_ERR_INVALID_ARGUMENT
+
+
+def test_decode_noalloc_scratch_limit():
+    # one split per head needs B * H_q * (d + 2) * 4 bytes of the 64 MiB
+    # scratch: 129056 bf16 sequence-heads at d = 128 do not fit (rejected
+    # before any HIP call)
+    far = 1 << 40
+    rows_max = (64 << 20) // ((128 + 2) * 4)
+    assert rows_max == 129055
+    big = dict(q=far, k=2 * far, v=3 * far, seqlens=0, out=4 * far, lse=0, S_max=64, H_q=1, H_kv=1)
+    assert _call_dec_noalloc(B=rows_max + 1, **big) == sqa.SQA_ERR_UNSUPPORTED
+    assert _call_dec_noalloc(B=0, q=0, k=0, v=0, out=0) == sqa.SQA_OK
+    assert _call_dec_noalloc(d=96) == sqa.SQA_ERR_UNSUPPORTED
