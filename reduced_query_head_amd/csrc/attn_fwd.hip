@@ -38,6 +38,11 @@
 //  * Causal: tiles above a wave's last row are skipped, diagonal tiles are
 //    masked per element; sequence tails: key rows are clamped for the loads
 //    and masked in the scores, query rows past S are never stored.
+//  * Grids too small to fill the chip (non-causal, d = 64: fewer than two
+//    8-wave workgroups per CU) split each workgroup's key range in two:
+//    waves w and w + 4 take the same query item, one half of the keys each,
+//    and merge their running maxima, row sums and O^T through LDS at the end
+//    (twice the workgroups, each with half the key loop).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -63,7 +68,7 @@ struct Bf16Params {
   int R;
   int n_groups;          // B * H_kv
   int n_items;           // R * ceil(S / kRows), items per group
-  int chunks;            // ceil(n_items / WAVES), workgroups per group
+  int chunks;            // ceil(n_items / items per workgroup), workgroups per group
   float c;               // |scale| * log2(e), strictly positive
   uint32_t q_sign;       // 0x8000 when scale < 0: q is negated on load (exact)
   float* lse;            // optional [B, S, H_q] row log-normaliser (natural log)
@@ -76,20 +81,27 @@ struct Bf16Params {
 template <int D, int WAVES, int KEYS>
 constexpr int fwd_min_waves_per_simd() { return (D == 64 && WAVES == 8 && KEYS == 64) ? 4 : 2; }
 
-template <int D, bool CAUSAL, int WAVES, int KEYS>
+template <int D, bool CAUSAL, int WAVES, int KEYS, int KSPLIT>
 __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>())) void attn_fwd_bf16(Bf16Params p) {
   constexpr int KS = D / 16;      // MFMA k-steps over the head dimension
   constexpr int DB = D / 32;      // 32-row blocks of O^T
   constexpr int NB = KEYS / 32;  // 32-key blocks per tile
   constexpr int NT = KEYS / 16;  // 16-key MFMA steps of P.V per tile
   constexpr int TILE = KEYS * D; // elements per tile
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_k0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_k1[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_v0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds_v1[TILE];
+  constexpr int IPW = WAVES / KSPLIT;  // items per workgroup
+  static_assert(KSPLIT == 1 || (KSPLIT == 2 && KEYS == 64), "key split: two parts, 64-key tiles");
+  // one tile per key part in each buffer
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k0[KSPLIT * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k1[KSPLIT * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v0[KSPLIT * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v1[KSPLIT * TILE];
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave_id = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // with a key split, waves w and w + IPW take the same query item and the
+  // two halves of the workgroup's key range (merged at the end)
+  const int wave = KSPLIT == 1 ? wave_id : wave_id % IPW;
+  const int kpart = KSPLIT == 1 ? 0 : wave_id / IPW;
   const int half = lane >> 5;     // which half of the wave
   const int col = lane & 31;      // query column of this lane in S^T / O^T
   const int S = p.S;
@@ -103,24 +115,32 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
   const int b = grp / p.H_kv;
   const int g = grp % p.H_kv;
 
-  const int item = chunk * WAVES + wave;
+  const int item = chunk * IPW + wave;
   const bool active = item < p.n_items;
   const int pos0 = (item / p.R) * kRows;
   const int h = g * p.R + item % p.R;
 
-  const int last_item = min(chunk * WAVES + WAVES - 1, p.n_items - 1);
+  const int last_item = min(chunk * IPW + IPW - 1, p.n_items - 1);
   const int wg_last_pos = min((last_item / p.R) * kRows + kRows - 1, S - 1);
-  const int n_tiles = CAUSAL ? wg_last_pos / KEYS + 1 : (S + KEYS - 1) / KEYS;
+  const int wg_tiles = CAUSAL ? wg_last_pos / KEYS + 1 : (S + KEYS - 1) / KEYS;
+  // this wave's key part: tiles [t_first, t_first + n_tiles) of the
+  // workgroup's range; every wave runs part_steps steps (one barrier each)
+  const int part_steps = (wg_tiles + KSPLIT - 1) / KSPLIT;
+  const int t_first = kpart * part_steps;
+  const int n_tiles = KSPLIT == 1 ? wg_tiles : max(0, min(wg_tiles - t_first, part_steps));
 
   const int64_t kv_stride = p.kv_stride;
-  const uint16_t* k_base = p.k + (int64_t)b * S * kv_stride + g * D;
-  const uint16_t* v_base = p.v + (int64_t)b * S * kv_stride + g * D;
+  const uint16_t* k_base = p.k + (int64_t)b * S * kv_stride + g * D + (int64_t)t_first * KEYS * kv_stride;
+  const uint16_t* v_base = p.v + (int64_t)b * S * kv_stride + g * D + (int64_t)t_first * KEYS * kv_stride;
+  const int S_part = S - t_first * KEYS;   // keys from this part's first tile to the end
 
-  TileCopy<D, WAVES, KEYS> cp;
+  TileCopy<D, IPW, KEYS> cp;
   cp.init(kv_stride, wave, lane);
   // first K/V tile in flight while Q loads
-  cp.issue(k_base, kv_stride, S, (SQA_LDS uint16_t*)lds_k0, wave);
-  cp.issue(v_base, kv_stride, S, (SQA_LDS uint16_t*)lds_v0, wave);
+  if (KSPLIT == 1 || n_tiles > 0) {
+    cp.issue(k_base, kv_stride, S_part, (SQA_LDS uint16_t*)lds_k0 + kpart * TILE, wave);
+    cp.issue(v_base, kv_stride, S_part, (SQA_LDS uint16_t*)lds_v0 + kpart * TILE, wave);
+  }
 
   // Q^T as the B operand: lane holds query (pos0 + col), head dims
   // ks*16 + half*8 ... +7.
@@ -140,7 +160,7 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
   // per-lane LDS element offsets (tile-relative), independent of the tile
   int k_off[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) k_off[ks] = tile_off<D>(col, ks * 16 + half * 8);
+  for (int ks = 0; ks < KS; ++ks) k_off[ks] = kpart * TILE + tile_off<D>(col, ks * 16 + half * 8);
   // transposed V reads: lane (within its 16-lane group) supplies the address
   // of row e = (lane%16)/4 and columns 4*(lane%4) ... +3 of a 4 x 16 block;
   // the hardware returns to lane i the 4 rows of column i.
@@ -153,7 +173,7 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
       for (int j = 0; j < 2; ++j) {
         const int row = 4 * half + 8 * j + e;
         const int cc = db * 32 + (grp16 & 1) * 16 + 4 * c4;
-        v_off[db][j] = tile_off<D>(row, cc);
+        v_off[db][j] = kpart * TILE + tile_off<D>(row, cc);
       }
   }
 
@@ -167,19 +187,20 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
   const int wave_last = pos0 + kRows - 1;
 
   auto step = [&](int t, SQA_LDS uint16_t* kt_cur, SQA_LDS uint16_t* vt_cur, SQA_LDS uint16_t* kt_nxt, SQA_LDS uint16_t* vt_nxt) {
-    const int kv0 = t * KEYS;
+    const int kv0l = t * KEYS;                // first key of the tile within the part
+    const int kv0 = t_first * KEYS + kv0l;    // and within the sequence
     wait_copies();     // this wave's copies of tile t landed
     __syncthreads();   // everyone's copies landed; tile t-1 fully consumed
     // copies of tile t+1 into the other buffers; issued after this tile's
     // K.Q^T MFMAs so that their issue overlaps matrix work
     auto copy_next = [&]() {
       if (t + 1 < n_tiles) {
-        const int64_t nxt = (int64_t)(kv0 + KEYS) * kv_stride;
-        cp.issue(k_base + nxt, kv_stride, S - kv0 - KEYS, kt_nxt, wave);
-        cp.issue(v_base + nxt, kv_stride, S - kv0 - KEYS, vt_nxt, wave);
+        const int64_t nxt = (int64_t)(kv0l + KEYS) * kv_stride;
+        cp.issue(k_base + nxt, kv_stride, S_part - kv0l - KEYS, kt_nxt + kpart * TILE, wave);
+        cp.issue(v_base + nxt, kv_stride, S_part - kv0l - KEYS, vt_nxt + kpart * TILE, wave);
       }
     };
-    if (!active || (CAUSAL && kv0 > wave_last)) {  // no work on this tile
+    if ((KSPLIT > 1 && t >= n_tiles) || !active || (CAUSAL && kv0 > wave_last)) {  // no work on this tile
       copy_next();
       return;
     }
@@ -272,9 +293,49 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
     __builtin_amdgcn_s_setprio(0);
     l_run += psum;
   };
-  for (int t = 0; t < n_tiles; t += 2) {
+  const int steps = KSPLIT == 1 ? n_tiles : part_steps;
+  for (int t = 0; t < steps; t += 2) {
     step(t, (SQA_LDS uint16_t*)lds_k0, (SQA_LDS uint16_t*)lds_v0, (SQA_LDS uint16_t*)lds_k1, (SQA_LDS uint16_t*)lds_v1);
-    if (t + 1 < n_tiles) step(t + 1, (SQA_LDS uint16_t*)lds_k1, (SQA_LDS uint16_t*)lds_v1, (SQA_LDS uint16_t*)lds_k0, (SQA_LDS uint16_t*)lds_v0);
+    if (t + 1 < steps) step(t + 1, (SQA_LDS uint16_t*)lds_k1, (SQA_LDS uint16_t*)lds_v1, (SQA_LDS uint16_t*)lds_k0, (SQA_LDS uint16_t*)lds_v0);
+  }
+
+  if constexpr (KSPLIT == 2) {
+    // merge the two key parts of each item: part 1 hands its running
+    // maximum, row sum and unnormalised O^T to part 0 through LDS (the tile
+    // buffers, free once every wave is past its last tile); part 0 rescales
+    // both to the larger maximum and adds them (a part with no visible key
+    // holds m = -inf, l = 0, O = 0 and adds nothing)
+    // items 0, 1 exchange O^T through lds_k0, items 2, 3 through lds_k1
+    // ([2][DB*16][64] floats each), the statistics through lds_v0
+    static_assert(IPW == 4 && 2 * 64 * 16 * DB * 4 <= KSPLIT * TILE * 2, "O exchange fits two K buffers");
+    wait_copies();
+    __syncthreads();
+    SQA_LDS float* xo = (SQA_LDS float*)(wave < 2 ? (SQA_LDS uint16_t*)lds_k0 : (SQA_LDS uint16_t*)lds_k1) +
+                        (wave & 1) * DB * 16 * 64;
+    SQA_LDS float* xm = (SQA_LDS float*)lds_v0;   // [IPW][2][64]
+    if (kpart == 1 && active) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[(db * 16 + r) * 64 + lane] = o[db][r];
+      xm[(wave * 2) * 64 + lane] = m_run;
+      xm[(wave * 2 + 1) * 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (kpart == 1) return;
+    if (active) {
+      const float m1 = xm[(wave * 2) * 64 + lane];
+      const float l1 = xm[(wave * 2 + 1) * 64 + lane];
+      const float m_new = fmaxf(m_run, m1);
+      const float a0 = __builtin_amdgcn_exp2f(m_run - m_new);
+      const float a1 = __builtin_amdgcn_exp2f(m1 - m_new);
+      l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + xo[(db * 16 + r) * 64 + lane] * a1;
+      m_run = m_new;
+    }
   }
 
   if (!active) return;
@@ -345,7 +406,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
 
 
 
-template <int D, bool CAUSAL, int WAVES, int KEYS>
+template <int D, bool CAUSAL, int WAVES, int KEYS, int KSPLIT = 1>
 hipError_t launch_bf16_w(const LaunchArgs& a) {
   Bf16Params p;
   p.q = (const uint16_t*)a.q;
@@ -359,14 +420,14 @@ hipError_t launch_bf16_w(const LaunchArgs& a) {
   p.n_groups = (int)(a.B * a.H_kv);
   const int n_pos_blocks = (int)((a.S + kRows - 1) / kRows);
   p.n_items = p.R * n_pos_blocks;
-  p.chunks = (p.n_items + WAVES - 1) / WAVES;
+  p.chunks = (p.n_items + WAVES / KSPLIT - 1) / (WAVES / KSPLIT);
   p.c = a.c;
   p.q_sign = a.negate_q ? 0x8000u : 0u;
   p.lse = a.lse;
   p.q_stride = a.q_stride;
   p.kv_stride = a.kv_stride;
   const int64_t grid = (int64_t)p.n_groups * p.chunks;
-  hipLaunchKernelGGL((attn_fwd_bf16<D, CAUSAL, WAVES, KEYS>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
+  hipLaunchKernelGGL((attn_fwd_bf16<D, CAUSAL, WAVES, KEYS, KSPLIT>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
                      (hipStream_t)a.stream, p);
   return hipGetLastError();
 }
@@ -378,8 +439,11 @@ constexpr int kCUs = 256;
 // - d = 128: 8 waves, 128-key tiles; 231 VGPRs, so one workgroup per CU
 //   (2 waves per SIMD); taken from 512 workgroups on.
 // - d = 64: 8 waves, 64-key tiles, held to 128 VGPRs so that two workgroups
-//   share a CU (4 waves per SIMD); taken from 256 workgroups on.  Measured
-//   1.5-7 % faster than 128-key tiles at 2 waves per SIMD.
+//   share a CU (4 waves per SIMD); taken from 512 workgroups on.  Measured
+//   1.5-7 % faster than 128-key tiles at 2 waves per SIMD.  Non-causal
+//   grids of 128-511 such workgroups split the key range in two (twice the
+//   workgroups): at S = 4096, B = 2, the 4/4 heads went from 0.0544 to
+//   0.0430 ms and the 8/4 heads from 0.0789 to 0.0764 ms.
 // - d = 32: 8 waves, 128-key tiles (126 VGPRs, two workgroups per CU); taken
 //   from 512 workgroups on.  2-5 % faster than the 4-wave shape.
 template <int D, bool CAUSAL>
@@ -387,7 +451,10 @@ hipError_t launch_bf16_t(const LaunchArgs& a) {
   const int64_t items = (int64_t)(a.H_q / a.H_kv) * ((a.S + kRows - 1) / kRows);
   const int64_t wgs8 = a.B * a.H_kv * ((items + 7) / 8);
   if constexpr (D == 64) {
-    if (wgs8 >= kCUs) return launch_bf16_w<D, CAUSAL, 8, 64>(a);
+    if (wgs8 >= 2 * kCUs) return launch_bf16_w<D, CAUSAL, 8, 64>(a);
+    if constexpr (!CAUSAL) {
+      if (wgs8 * 2 >= kCUs) return launch_bf16_w<D, CAUSAL, 8, 64, 2>(a);
+    }
   } else {
     if (wgs8 >= 2 * kCUs) return launch_bf16_w<D, CAUSAL, 8, 128>(a);
   }

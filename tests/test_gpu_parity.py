@@ -214,3 +214,46 @@ def test_lse_full_size_sampled(name, variant):
     got = lse[:, torch.from_numpy(rows).to(lse.device)].cpu().numpy()
     del o, lse, dq, dk, dv
     _check_lse(got, oracle.lse(q, k, float(np.float32(w.scale)), causal=w.causal, rows=rows), "bf16", name)
+
+
+# Non-causal d = 64 grids of 128-511 eight-wave workgroups, where every
+# workgroup splits its key range in two and merges the halves: an odd tile
+# count with a 32-key last tile, a 4-key last tile with two heads per group,
+# one tile per workgroup (the second half has no keys), two tiles with a
+# partial second one, the S = 4096 4/4 shape whole, and four heads per group.
+KEY_SPLIT = [
+    (1, 4000, 8, 8, 64), (2, 2500, 8, 4, 64), (16, 64, 8, 8, 64), (32, 100, 4, 4, 64),
+    (2, 4096, 4, 4, 64), (2, 3000, 16, 4, 64),
+]
+
+
+@pytest.mark.parametrize("B,S,H_q,H_kv,d", KEY_SPLIT)
+def test_key_split_full_output_and_lse(B, S, H_q, H_kv, d):
+    _say(f"key split B={B} S={S} H={H_q}/{H_kv} d={d}")
+    seed = 4400 + S * 3 + H_q + B
+    q = inputs.normal(seed, 0, (B, S, H_q, d), "bf16", 0.5)
+    k = inputs.normal(seed, 1, (B, S, H_kv, d), "bf16", 0.5)
+    v = inputs.normal(seed, 2, (B, S, H_kv, d), "bf16", 0.5)
+    dq, dk, dv = gpu_util.to_device(q), gpu_util.to_device(k), gpu_util.to_device(v)
+    for scale in (1.0 / math.sqrt(d), -0.3):
+        o, lse = sqa.attn_fwd(dq, dk, dv, scale=scale, causal=False, return_lse=True)
+        torch.cuda.synchronize()
+        sc = float(np.float32(scale))
+        st = check(gpu_util.to_host_f64(o), oracle.attention(q, k, v, sc), "bf16", f"key split scale={scale}")
+        _check_lse(lse.cpu().numpy(), oracle.lse(q, k, sc), "bf16", f"key split lse scale={scale}")
+        _say(f"  scale={scale} {st}")
+
+
+def test_key_split_peaked_second_half():
+    """The largest scores sit in the second half of the keys (positions
+    scaled by 8 there), so the merge must rescale the first half's sums by
+    a large factor."""
+    B, S, H_q, H_kv, d = 16, 256, 8, 8, 64
+    q = inputs.normal(4501, 0, (B, S, H_q, d), "bf16", 0.5)
+    k = inputs.normal(4501, 1, (B, S, H_kv, d), "bf16", 0.5)
+    v = inputs.normal(4501, 2, (B, S, H_kv, d), "bf16", 0.5)
+    pos = np.arange(S // 2, S, 9, dtype=np.int64)
+    inputs.scale_positions_bf16(k, pos, 8.0)
+    got = gpu_util.to_host_f64(gpu_util.run(q, k, v, 1.0, False))
+    ref = oracle.attention(q, k, v, 1.0)
+    _say(f"  {check(got, ref, 'bf16', 'key split peaked')}")
