@@ -18,7 +18,8 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        path = lib_path()
+        # a test may point at another build of the same source (sanitizers)
+        path = os.environ.get("SQA_INPUTS_LIB") or lib_path()
         if not os.path.exists(path):
             build()
         lib = ctypes.CDLL(path)

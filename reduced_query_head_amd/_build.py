@@ -5,7 +5,8 @@ import subprocess
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["csrc/api.cpp", "csrc/attn_fwd.hip", "csrc/attn_bwd.hip", "csrc/attn_decode.hip", "csrc/layer.cpp"]
+SOURCES = ["csrc/api.cpp", "csrc/plan.cpp", "csrc/attn_fwd.hip", "csrc/attn_bwd.hip", "csrc/attn_decode.hip",
+           "csrc/layer.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
     # no packed-fp32 instructions in device code

@@ -45,11 +45,10 @@ namespace {
 
 using namespace dev;
 
-constexpr int kRows32 = 32;  // query rows (dq) or keys (dk/dv) per wave
+constexpr int kRows32 = kBwdRows;  // query rows (dq) or keys (dk/dv) per wave
 constexpr int kTile = 64;    // K/V tile (dq) and Q/dO tile (dk/dv) length
-constexpr int kWaves = 4;
+constexpr int kWaves = kBwdWaves;
 
-__host__ __device__ constexpr int64_t pad64(int64_t s) { return (s + 63) / 64 * 64; }
 
 struct BwdParams {
   const uint16_t* q;
@@ -657,20 +656,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32(const float* q, const float*
   }
 }
 
-// dk/dv grid: one workgroup per (group, key block), or, for sequences of at
-// least 64 key blocks, 32-block chunks dealt to the 8 XCDs (the grid padded
-// to whole rounds of 8 chunks).
-int64_t dkdv_layout(int64_t n_groups, int64_t key_blocks, int* kb_chunk) {
-  constexpr int kChunk = 32;
-  if (key_blocks < 2 * kChunk) {
-    *kb_chunk = 0;
-    return n_groups * key_blocks;
-  }
-  *kb_chunk = kChunk;
-  const int64_t units = n_groups * ((key_blocks + kChunk - 1) / kChunk);
-  return (units + 7) / 8 * 8 * kChunk;
-}
-
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_bf16_t(const BwdArgs& a) {
   BwdParams p;
@@ -738,17 +723,6 @@ hipError_t launch_bwd_f32_t(const BwdArgs& a) {
 }
 
 }  // namespace
-
-int64_t bwd_workspace_bytes(int64_t B, int64_t S, int32_t H_q) { return 2 * B * (int64_t)H_q * pad64(S) * 4; }
-
-int64_t bwd_grid_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv) {
-  const int64_t items = (int64_t)(H_q / H_kv) * ((S + kRows32 - 1) / kRows32);
-  const int64_t a = B * H_kv * ((items + kWaves - 1) / kWaves);
-  int kb_chunk;
-  const int64_t b = dkdv_layout(B * H_kv, (S + kWaves * kRows32 - 1) / (kWaves * kRows32), &kb_chunk);
-  const int64_t c = (B * H_q * pad64(S) * 8 + 255) / 256;
-  return a > b ? (a > c ? a : c) : (b > c ? b : c);
-}
 
 hipError_t launch_attn_bwd(const BwdArgs& a) {
   if (a.dtype == 0) {

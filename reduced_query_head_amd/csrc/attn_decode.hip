@@ -42,7 +42,7 @@ namespace {
 
 using namespace dev;
 
-constexpr int kBlk = 32;          // keys per block (one S^T MFMA tile)
+constexpr int kBlk = kDecodeBlk;  // keys per block (one S^T MFMA tile)
 constexpr int kWavesDec = 4;      // waves per workgroup (independent)
 constexpr float kLazyLog2D = 8.0f;
 
@@ -411,49 +411,6 @@ hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& plan) {
 }
 
 }  // namespace
-
-// Split plan: about 8 waves per wave slot of the chip (8 per CU), so that
-// the last round is a small part of the work even when many splits are
-// empty (short caches).  Splits shorter than 512 keys are lengthened
-// towards 512 as long as at least 2 waves per slot remain: short splits
-// spend a larger share of their time starting up and add merge work (512
-// instead of 256 made the 32/8 and 16/8 head configurations of a 4 x 128K
-// cache 1-3 % faster).  Each split has at least 64 keys, and at least 16
-// keys per query head it serves, so the fp32 partial results written per
-// split stay within a few percent of the cache bytes it reads.
-DecodePlan decode_plan(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d, int64_t max_workspace) {
-  DecodePlan pl;
-  const int64_t R = H_q / H_kv;
-  pl.head_blocks = (int)((R + 31) / 32);
-  const int64_t units = B * H_kv * pl.head_blocks;
-  const int64_t target_waves = 8 * 8 * 256, floor_waves = 2 * 8 * 256;
-  const int64_t heads_per_wave = R < 32 ? R : 32;
-  int64_t len = units > 0 ? (S_max * units + target_waves - 1) / target_waves : S_max;
-  if (len < 512 && units > 0) {
-    const int64_t len_floor = S_max * units / floor_waves;  // keeps >= floor_waves waves
-    len = len_floor < 512 ? (len_floor > len ? len_floor : len) : 512;
-  }
-  if (len < 64) len = 64;
-  if (len < 16 * heads_per_wave) len = 16 * heads_per_wave;
-  len = (len + kBlk - 1) / kBlk * kBlk;
-  // a workspace bound: at most max_workspace / (bytes per split of every
-  // head) splits, so each split covers at least S_max / that many keys
-  const int64_t per_split = B * H_q * (int64_t)(d + 2) * 4;
-  if (max_workspace > 0 && per_split > 0 && S_max > 0) {
-    const int64_t max_splits = max_workspace / per_split;
-    if (max_splits >= 1) {
-      int64_t fit = (S_max + max_splits - 1) / max_splits;
-      fit = (fit + kBlk - 1) / kBlk * kBlk;
-      if (fit > len) len = fit;
-    }
-  }
-  pl.split_len = (int)len;
-  pl.n_splits = (int)(S_max > 0 ? (S_max + len - 1) / len : 1);
-  pl.part_o_bytes = B * H_q * (int64_t)pl.n_splits * d * 4;
-  pl.workspace_bytes = pl.part_o_bytes + B * H_q * (int64_t)pl.n_splits * 2 * 4;
-  pl.n_waves = units * pl.n_splits;
-  return pl;
-}
 
 namespace {
 

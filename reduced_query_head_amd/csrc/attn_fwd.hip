@@ -54,7 +54,7 @@ namespace {
 
 using namespace dev;
 
-constexpr int kRows = 32;         // query positions per item (one wave)
+constexpr int kRows = kFwdRows;   // query positions per item (one wave)
 constexpr float kLazyLog2 = 8.0f;  // running-max slack before a rescale (log2 units)
 
 struct Bf16Params {
@@ -474,12 +474,6 @@ hipError_t launch_f32_t(const LaunchArgs& a) {
 }
 
 }  // namespace
-
-int64_t bf16_grid_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv) {
-  const int64_t R = H_q / H_kv;
-  const int64_t items = R * ((S + kRows - 1) / kRows);
-  return B * H_kv * ((items + 3) / 4);
-}
 
 hipError_t launch_attn_fwd(const LaunchArgs& a) {
   if (a.dtype == 0) {

@@ -7,6 +7,17 @@
 
 namespace sqa {
 
+// Work decomposition shared by the kernels and the host plans (plan.cpp).
+constexpr int kFwdRows = 32;      // query positions per forward item (one wave)
+constexpr int kBwdRows = 32;      // query rows (dq) or keys (dk/dv) per backward wave
+constexpr int kBwdWaves = 4;      // waves of a dq workgroup (a dk/dv workgroup has twice as many)
+constexpr int kDkdvChunk = 32;    // key blocks of one group an XCD takes in a row (long sequences)
+constexpr int kDecodeBlk = 32;    // keys per decode block (one S^T MFMA tile)
+constexpr int64_t kLayerGemmWorkspace = (int64_t)32 << 20;   // bytes offered to the GEMM library
+
+// rows padded to the backward's 64-row tiles
+__host__ __device__ constexpr int64_t pad64(int64_t s) { return (s + 63) / 64 * 64; }
+
 struct LaunchArgs {
   const void* q;
   const void* k;
@@ -55,6 +66,8 @@ struct BwdArgs {
 
 hipError_t launch_attn_bwd(const BwdArgs& a);
 int64_t bwd_workspace_bytes(int64_t B, int64_t S, int32_t H_q);
+// dk/dv grid size; *kb_chunk = key blocks per XCD chunk (0: no chunking)
+int64_t dkdv_layout(int64_t n_groups, int64_t key_blocks, int* kb_chunk);
 int64_t bwd_grid_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv);
 int64_t bf16_grid_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv);
 

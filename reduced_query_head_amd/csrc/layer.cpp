@@ -24,7 +24,7 @@
 namespace sqa {
 namespace {
 
-constexpr int64_t kGemmWorkspace = 32ll << 20;   // bytes of workspace offered to hipBLASLt
+constexpr int64_t kGemmWorkspace = kLayerGemmWorkspace;   // bytes of workspace offered to hipBLASLt
 
 struct GemmPlan {
   hipblasLtMatmulDesc_t desc = nullptr;
@@ -91,19 +91,7 @@ bool gemm_nt(int dev, hipblasLtHandle_t h, hipStream_t stream, const void* X, co
                          pl->ws, stream) == HIPBLAS_STATUS_SUCCESS;
 }
 
-int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
-
 }  // namespace
-
-LayerPlan layer_plan(int64_t B, int64_t S, int32_t H_q, int32_t H_kv, int32_t d) {
-  LayerPlan p;
-  p.n_qkv = ((int64_t)H_q + 2 * (int64_t)H_kv) * d;
-  p.qkv_bytes = round_up(B * S * p.n_qkv * 2, 256);
-  p.attn_bytes = round_up(B * S * (int64_t)H_q * d * 2, 256);
-  p.gemm_ws_bytes = kGemmWorkspace;
-  p.workspace_bytes = p.qkv_bytes + p.attn_bytes + p.gemm_ws_bytes;
-  return p;
-}
 
 hipError_t launch_layer_fwd(const LayerArgs& a, bool* lib_error) {
   *lib_error = false;

@@ -11,6 +11,13 @@ import reduced_query_head_amd as sqa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
+# The host sanitizer test reruns this file against a host-only build of the
+# same C-ABI source whose kernel launchers are stubs (tests/sanitize); every
+# call below then goes to that build.
+STUB_LIB = os.environ.get("SQA_TEST_STUB_LIB")
+if STUB_LIB:
+    sqa.load_library(STUB_LIB)
+
 
 def _declared_functions():
     text = open(os.path.join(ROOT, "include", "sqa.h")).read()
@@ -248,3 +255,34 @@ def test_decode_noalloc_scratch_limit():
     assert _call_dec_noalloc(B=rows_max + 1, **big) == sqa.SQA_ERR_UNSUPPORTED
     assert _call_dec_noalloc(B=0, q=0, k=0, v=0, out=0) == sqa.SQA_OK
     assert _call_dec_noalloc(d=96) == sqa.SQA_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# Only against the stub build: valid calls reach the launcher with the
+# arguments the kernels expect (no GPU involved).
+
+
+def _stub_last():
+    lib = sqa.load_library()
+    c, neg, qs, kvs, ws = (ctypes.c_float(), ctypes.c_int(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int())
+    kind = lib.sqa_stub_last(ctypes.byref(c), ctypes.byref(neg), ctypes.byref(qs), ctypes.byref(kvs),
+                             ctypes.byref(ws))
+    return kind, c.value, neg.value, qs.value, kvs.value, ws.value
+
+
+@pytest.mark.skipif(not STUB_LIB, reason="needs the host-only stub build of the C ABI")
+def test_stub_valid_calls_reach_launchers():
+    lib = sqa.load_library()
+    lib.sqa_stub_reset()
+    log2e = 1.4426950408889634
+    assert _call(H_q=8, H_kv=2, d=128, scale=-0.25) == sqa.SQA_OK
+    kind, c, neg, qs, kvs, _ = _stub_last()
+    assert kind == 1 and neg == 1 and qs == 8 * 128 and kvs == 2 * 128
+    assert abs(c - 0.25 * log2e) <= 1e-6
+    assert _call(scale=0.0) == sqa.SQA_OK and 0 < _stub_last()[1] < 1e-20   # scale 0: a tiny positive factor
+    assert _call_bwd() == sqa.SQA_OK and _stub_last()[0] == 2 and _stub_last()[5] == 1
+    assert _call_dec() == sqa.SQA_OK and _stub_last()[0] == 3 and _stub_last()[5] == 1
+    assert _call_dec_noalloc() == sqa.SQA_OK and _stub_last()[0] == 4 and _stub_last()[5] == 0
+    assert _call_layer() == sqa.SQA_OK and _stub_last()[0] == 5 and _stub_last()[5] == 1
+    lib.sqa_stub_reset()
+    assert _call(H_q=6, H_kv=4) == sqa.SQA_ERR_INVALID_ARGUMENT and _stub_last()[0] == 0   # rejected: no launch
