@@ -68,21 +68,31 @@ def time_variant(sqa, torch, w, variant, steps, warmup):
     for _ in range(warmup):
         sqa.attn_fwd(dq, dk, dv, out=out, scale=w.scale, causal=w.causal, stream=stream)
     torch.cuda.synchronize()
-    # per-launch HIP events on the launch stream, plus the whole timed region
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    # the timed region: back-to-back launches between two HIP events on the
+    # launch stream (nothing else enqueued in between)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    ev[0].record(stream)
+    e0.record(stream)
     for i in range(steps):
+        sqa.attn_fwd(dq, dk, dv, out=out, scale=w.scale, causal=w.causal, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = e0.elapsed_time(e1)
+    # then the spread of single launches: an event after each launch of a
+    # second, shorter pass (the events add a little time to each interval)
+    n_per = min(steps, 20)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_per + 1)]
+    ev[0].record(stream)
+    for i in range(n_per):
         sqa.attn_fwd(dq, dk, dv, out=out, scale=w.scale, causal=w.causal, stream=stream)
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_launch = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    per_launch = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(n_per))
     flops = algorithmic_flops(w.B, w.S, v.H_q, w.d, w.causal)
-    total_ms = ev[0].elapsed_time(ev[steps])
     res = dict(H_q=v.H_q, H_kv=v.H_kv, flops=flops, ms_per_step=total_ms / steps,
-               avg_launch_ms=sum(per_launch) / steps, median_launch_ms=sorted(per_launch)[steps // 2],
-               min_launch_ms=min(per_launch), max_launch_ms=max(per_launch), wall_s=wall)
+               avg_launch_ms=total_ms / steps, median_launch_ms=per_launch[n_per // 2],
+               min_launch_ms=per_launch[0], max_launch_ms=per_launch[-1], wall_s=wall)
     res["tflops"] = flops / (res["ms_per_step"] * 1e-3) / 1e12
     res["tokens_per_s"] = w.B * w.S / (res["ms_per_step"] * 1e-3)
     del dq, dk, dv, out
@@ -361,9 +371,10 @@ def _csv_rows(directory, suffix):
     return rows
 
 
-def summarize_trace(directory, kernel_re, skip, flops=None):
+def summarize_trace(directory, kernel_re, skip, flops=None, count=0):
     """Markdown summary of a rocprofv3 --kernel-trace CSV: per matching kernel,
-    the launch durations after the first `skip` launches (the warm-ups)."""
+    the durations of `count` launches (all, if 0) after the first `skip`
+    launches (the warm-ups)."""
     rows = [r for r in _csv_rows(directory, "kernel_trace.csv") if re.search(kernel_re, r["Kernel_Name"])]
     by_name = {}
     for r in rows:
@@ -373,7 +384,7 @@ def summarize_trace(directory, kernel_re, skip, flops=None):
     stats = {}
     for name, ts in by_name.items():
         ts.sort()
-        d = sorted((e - b) / 1e6 for b, e in ts[skip:])
+        d = sorted((e - b) / 1e6 for b, e in (ts[skip:skip + count] if count else ts[skip:]))
         if not d:
             continue
         mean, med = sum(d) / len(d), d[len(d) // 2]
@@ -455,6 +466,33 @@ def traffic_summary(fetch_dir, write_dir, kernel_re, skip, w, variant):
         f"measured/algorithmic: reads {fb / alg_r:.2f}x, writes {wb / alg_w:.2f}x"])
 
 
+def mfma_summary(directory, kernel_re, skip, w, variant, launch_ms):
+    """MFMA occupancy and effective clock of one kernel from a rocprofv3 pass
+    over SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16,
+    GRBM_GUI_ACTIVE and GRBM_COUNT (summed over the chip per dispatch).  The
+    clock is GRBM_GUI_ACTIVE per XCD over the unprofiled launch time
+    `launch_ms` of the same workload (counter collection slows launches)."""
+    per, _ = summarize_counters([directory], kernel_re, skip)
+    mean = {k: sum(v) / len(v) for k, v in per.items()}
+    v = w.variant(variant)
+    flops = algorithmic_flops(w.B, w.S, v.H_q, w.d, w.causal)
+    simds, xcds = 1024, 8
+    busy_simd = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
+    active_xcd = mean["GRBM_GUI_ACTIVE"] / xcds
+    clk = active_xcd / (launch_ms * 1e-3)
+    share = busy_simd / active_xcd
+    lines = [counters_markdown(per, {}), "",
+             f"- MOPS x 512 = {mean['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:.4e} flop per launch; algorithmic "
+             f"{flops:.4e} ({mean['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / flops:.3f}x)",
+             f"- MFMA busy cycles per SIMD {busy_simd:.4e}; GRBM_GUI_ACTIVE per XCD {active_xcd:.4e}",
+             f"- MFMA busy share of active cycles: {100 * share:.1f} %",
+             f"- effective clock over the unprofiled launch time {launch_ms:.4f} ms: {clk / 1e9:.3f} GHz "
+             f"({100 * clk / 2.4e9:.1f} % of 2.4 GHz)",
+             f"- product {100 * share * clk / 2.4e9:.1f} % of the dense bf16 peak; the unprofiled launch time gives "
+             f"{100 * flops / (launch_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS:.1f} %"]
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -483,11 +521,13 @@ def main():
                     help="only run a plain device copy of 1 GiB (HBM counter calibration)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="run a plain 1 GiB device copy before the timed work (counter calibration in the same run)")
-    ap.add_argument("--summarize", choices=["trace", "counters", "traffic"],
+    ap.add_argument("--launch-ms", type=float, default=0.0, help="unprofiled launch time for --summarize mfma")
+    ap.add_argument("--summarize", choices=["trace", "counters", "traffic", "mfma"],
                     help="print a markdown summary of rocprofv3 CSV output instead of running (no GPU)")
     ap.add_argument("--dirs", default="", help="comma list of rocprofv3 output folders for --summarize")
     ap.add_argument("--kernel", default="attn_fwd_bf16", help="kernel-name regex for --summarize")
     ap.add_argument("--skip", type=int, default=0, help="launches of the kernel to leave out (warm-ups)")
+    ap.add_argument("--count", type=int, default=0, help="launches to summarize after the skipped ones (0 = all)")
     args = ap.parse_args()
 
     if args.summarize:
@@ -497,7 +537,9 @@ def main():
         if args.summarize == "trace":
             v = w.variant(args.variant)
             print(summarize_trace(dirs[0], args.kernel, args.skip,
-                                  algorithmic_flops(w.B, w.S, v.H_q, w.d, w.causal)))
+                                  algorithmic_flops(w.B, w.S, v.H_q, w.d, w.causal), args.count))
+        elif args.summarize == "mfma":
+            print(mfma_summary(dirs[0], args.kernel, args.skip, w, args.variant, args.launch_ms))
         elif args.summarize == "counters":
             print(counters_markdown(*summarize_counters(dirs, args.kernel, args.skip)))
         else:
@@ -574,7 +616,7 @@ def main():
                 e["sqa_speedup"] = round(r["ms_per_step"] / rs[first]["ms_per_step"], 3) if k != first else 1.0
                 e["ideal_speedup"] = round(r["H_q"] / rs[first]["H_q"], 3)
                 longctx[wn][k] = e
-    sweep = time_sweep(sqa, torch, 100, 10) if args.sweep == "auto" else None
+    sweep = time_sweep(sqa, torch, 200, 20) if args.sweep == "auto" else None
     bwd = (time_backward(sqa, torch, w, args.variant, max(3, args.steps // 2), args.warmup)
            if args.backward == "auto" and w.dtype == "bf16" else None)
     dec = time_decode(sqa, torch, args.decode_workload, 20, 3) if args.decode == "auto" else None
