@@ -182,7 +182,8 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
   for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
   float m_run = -__builtin_inff();
   float l_run = 0.f;
-  // Row sums on the matrix cores (d = 128): per P.V step one
+  // Row sums on the matrix cores (d = 128, and the non-causal 8-wave d = 64
+  // shape, whose register budget allows it): per P.V step one
   // v_mfma_f32_16x16x32_bf16 takes the bf16 probabilities as its B operand
   // (lane l supplies column l % 16, k-group l / 16, i.e. query l % 32 and key
   // half l / 32) and a 0/1 A operand that, for output rows 0-7, selects the
@@ -191,8 +192,9 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
   // keys of query n (rows 0-7) or n + 16 (rows 8-15), accumulated over the
   // whole key loop.  This replaces four v_dot2 per step (32 VALU
   // instructions per 128-key tile) with one short MFMA; measured 0.2-0.8 %
-  // faster on the 32K-200K workloads.
-  constexpr bool ROWMFMA = D == 128 && KSPLIT == 1;
+  // faster on the 32K-200K workloads and 3-4 % at d = 64 (S = 4096 and 32K,
+  // non-causal), where the softmax's VALU work is the tighter bound.
+  constexpr bool ROWMFMA = D == 128 || (D == 64 && !CAUSAL && WAVES == 8);
   f32x4 lsum = (f32x4){0.f, 0.f, 0.f, 0.f};
   bf16x8 rs_sel;
   {
@@ -328,6 +330,14 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
     if (t + 1 < steps) step(t + 1, (SQA_LDS uint16_t*)lds_k1, (SQA_LDS uint16_t*)lds_v1, (SQA_LDS uint16_t*)lds_k0, (SQA_LDS uint16_t*)lds_v0);
   }
 
+  if constexpr (ROWMFMA) {
+    // move each query's row sum to its own lanes (lanes 16-31 and 32-47
+    // swap) while every lane of the wave is active; the two lanes of a query
+    // each keep half of it (exact), as the v_dot2 path's partial sums
+    const int src = (lane >= 16 && lane < 48) ? (lane ^ 48) : lane;
+    l_run = 0.5f * __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(lsum[0])));
+  }
+
   if constexpr (KSPLIT == 2) {
     // merge the two key parts of each item: part 1 hands its running
     // maximum, row sum and unnormalised O^T to part 0 through LDS (the tile
@@ -368,16 +378,9 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
   }
 
   if (!active) return;
-  float l_tot;
-  if constexpr (ROWMFMA) {
-    // lane l needs its own query's sum: lanes 16-31 and 32-47 swap (while
-    // every lane of the wave is still active)
-    const int src = (lane >= 16 && lane < 48) ? (lane ^ 48) : lane;
-    l_tot = __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(lsum[0])));
-  }
   const int out_pos = pos0 + col;
   if (out_pos >= S) return;  // lanes l and l^32 share out_pos, so pairs leave together
-  if constexpr (!ROWMFMA) l_tot = wave_pair_sum(l_run);
+  const float l_tot = wave_pair_sum(l_run);
   const float inv = 1.0f / l_tot;
   // log of the row normaliser: scores entered the softmax as s*c with
   // c = scale*log2(e), so ln(sum_j exp(scale*s_j)) = ln2 * (m + log2(l))
