@@ -88,6 +88,13 @@ typedef enum {
  * call, and leave out untouched.  SQA_ERR_HIP reports a launch the runtime
  * refused.  Faults during execution surface at the caller's next
  * synchronisation on the stream.
+ *
+ * Speed: bf16 runs on MFMA kernels (the performance path).  fp32 runs on
+ * plain VALU kernels, one thread per query row (or, in the backward, per
+ * key), each looping over its keys (queries) in fp32.  They are meant for
+ * exactness checks at small sizes.  The size limits are the same as for
+ * bf16, but their time grows as S^2 per row, so they become impractically
+ * slow beyond a few thousand positions.
  */
 sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, void* out, int64_t B,
                         int64_t S, int32_t H_q, int32_t H_kv, int32_t d, sqa_dtype dtype,
