@@ -125,3 +125,51 @@ def test_noalloc_fp32_and_empty_caches():
     ow, lw, on, lnn = _both(q, k, v, ln, 0.1, None)
     assert np.array_equal(_bits(ow), _bits(on))
     assert np.isneginf(lnn[0].cpu().numpy()).all()
+
+
+def test_noalloc_under_graph_capture():
+    """The callers this entry point is for include code under HIP graph
+    capture: the call is captured once (after eager warm-up calls), the graph
+    is replayed with fresh cache contents copied into the captured buffers,
+    and every replay equals an eager call of the same entry point bitwise."""
+    B, S_max, H_q, H_kv, d = 3, 2000, 16, 4, 128
+    lens = torch.tensor([2000, 1234, 7], dtype=torch.int32, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(8107)
+
+    def fresh():
+        return [(0.5 * torch.randn(shape, device="cuda", generator=gen)).to(torch.bfloat16)
+                for shape in ((B, H_q, d), (B, S_max, H_kv, d), (B, S_max, H_kv, d))]
+
+    q, k, v = fresh()
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H_q), dtype=torch.float32, device="cuda")
+
+    def call(o, l):
+        st = sqa.attn_decode_noalloc_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), lens.data_ptr(), o.data_ptr(),
+                                         l.data_ptr(), B, S_max, H_q, H_kv, d, sqa.SQA_BF16, 1 / math.sqrt(d),
+                                         torch.cuda.current_stream().cuda_stream)
+        assert st == sqa.SQA_OK, sqa.status_string(st)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            call(out, lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out, lse)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = torch.empty_like(out), torch.empty_like(lse)
+    for rep in range(3):
+        for dst, src in zip((q, k, v), fresh()):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        call(ref_out, ref_lse)           # eager, same inputs
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), f"replay {rep}: out"
+        assert torch.equal(lse, ref_lse), f"replay {rep}: lse"
+        _say(f"no-alloc graph replay {rep}: equal")
