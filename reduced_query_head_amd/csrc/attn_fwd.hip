@@ -283,8 +283,15 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
     // From the exponentials to the last P.V MFMA this wave issues ahead of
     // the other wave on its SIMD (which is then in its K.Q^T or maximum
     // phase): measured 1-2 % faster at d = 128 and 2-7 % at d = 64, with the
-    // same results.
-    __builtin_amdgcn_s_setprio(2);
+    // same results.  With 8 waves at d = 128 the two waves of a SIMD (w and
+    // w + 4) take different levels, so that when both are in this phase one
+    // of them drains its P.V chain first instead of the two interleaving:
+    // a further 1.0-1.3 % at d = 128; at d = 64 (4 waves per SIMD) it cost
+    // 2-3 %, so that shape keeps one level.
+    if (WAVES == 8 && D == 128 && wave_id < WAVES / 2)
+      __builtin_amdgcn_s_setprio(1);
+    else
+      __builtin_amdgcn_s_setprio(2);
     const float neg_m = -m_run;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
