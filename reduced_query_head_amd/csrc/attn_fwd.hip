@@ -39,10 +39,10 @@
 //    masked per element; sequence tails: key rows are clamped for the loads
 //    and masked in the scores, query rows past S are never stored.
 //  * Grids too small to fill the chip (non-causal, d = 64: fewer than two
-//    8-wave workgroups per CU) split each workgroup's key range in two:
-//    waves w and w + 4 take the same query item, one half of the keys each,
-//    and merge their running maxima, row sums and O^T through LDS at the end
-//    (twice the workgroups, each with half the key loop).
+//    8-wave workgroups per CU) split each workgroup's key range in two or
+//    four parts: waves w, w + 4, ... take the same query item, one part of
+//    the keys each, and merge their running maxima, row sums and O^T
+//    through LDS at the end.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -77,9 +77,9 @@ struct Bf16Params {
 };
 
 // Waves per SIMD the register allocation must allow: 4 for the d = 64,
-// 8-wave, 64-key shape (two workgroups per CU), else 2.
+// 64-key shapes of 8 waves (two workgroups per CU) and 16 waves, else 2.
 template <int D, int WAVES, int KEYS>
-constexpr int fwd_min_waves_per_simd() { return (D == 64 && WAVES == 8 && KEYS == 64) ? 4 : 2; }
+constexpr int fwd_min_waves_per_simd() { return (D == 64 && WAVES >= 8 && KEYS == 64) ? 4 : 2; }
 
 template <int D, bool CAUSAL, int WAVES, int KEYS, int KSPLIT>
 __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>())) void attn_fwd_bf16(Bf16Params p) {
@@ -89,7 +89,8 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
   constexpr int NT = KEYS / 16;  // 16-key MFMA steps of P.V per tile
   constexpr int TILE = KEYS * D; // elements per tile
   constexpr int IPW = WAVES / KSPLIT;  // items per workgroup
-  static_assert(KSPLIT == 1 || (KSPLIT == 2 && KEYS == 64), "key split: two parts, 64-key tiles");
+  static_assert(KSPLIT == 1 || ((KSPLIT == 2 || KSPLIT == 4) && IPW == 4 && KEYS == 64),
+                "key split: two or four parts of four waves, 64-key tiles");
   // one tile per key part in each buffer
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k0[KSPLIT * TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t lds_k1[KSPLIT * TILE];
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
 
   const int lane = threadIdx.x & 63;
   const int wave_id = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // with a key split, waves w and w + IPW take the same query item and the
+  // with a key split, waves w, w + IPW, ... take the same query item and the
   // two halves of the workgroup's key range (merged at the end)
   const int wave = KSPLIT == 1 ? wave_id : wave_id % IPW;
   const int kpart = KSPLIT == 1 ? 0 : wave_id / IPW;
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
   // instructions per 128-key tile) with one short MFMA; measured 0.2-0.8 %
   // faster on the 32K-200K workloads and 3-4 % at d = 64 (S = 4096 and 32K,
   // non-causal), where the softmax's VALU work is the tighter bound.
-  constexpr bool ROWMFMA = D == 128 || (D == 64 && !CAUSAL && WAVES == 8);
+  constexpr bool ROWMFMA = D == 128 || (D == 64 && !CAUSAL && WAVES >= 8);
   f32x4 lsum = (f32x4){0.f, 0.f, 0.f, 0.f};
   bf16x8 rs_sel;
   {
@@ -345,42 +346,62 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
     l_run = 0.5f * __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(lsum[0])));
   }
 
-  if constexpr (KSPLIT == 2) {
-    // merge the two key parts of each item: part 1 hands its running
-    // maximum, row sum and unnormalised O^T to part 0 through LDS (the tile
-    // buffers, free once every wave is past its last tile); part 0 rescales
-    // both to the larger maximum and adds them (a part with no visible key
-    // holds m = -inf, l = 0, O = 0 and adds nothing)
-    // items 0, 1 exchange O^T through lds_k0, items 2, 3 through lds_k1
-    // ([2][DB*16][64] floats each), the statistics through lds_v0
-    static_assert(IPW == 4 && 2 * 64 * 16 * DB * 4 <= KSPLIT * TILE * 2, "O exchange fits two K buffers");
+  if constexpr (KSPLIT > 1) {
+    // merge the key parts of each item: parts 1 .. KSPLIT-1 hand their
+    // running maxima, row sums and unnormalised O^T to part 0 through LDS
+    // (the tile buffers, free once every wave is past its last tile); part
+    // 0 rescales all of them to the largest maximum and adds them in part
+    // order (a part with no visible key holds m = -inf, l = 0, O = 0 and adds
+    // nothing; part 0 always sees key 0).
+    // O^T slots of DB*16*64 floats: with two parts, items 0, 1 use lds_k0
+    // and items 2, 3 lds_k1, the statistics lds_v0; with four parts, part p
+    // uses lds_k0, lds_k1, lds_v0 for p = 1, 2, 3 (one slot per item), the
+    // statistics lds_v1 ([KSPLIT-1][IPW][2][64] floats).
+    constexpr int OX = DB * 16 * 64;
+    static_assert((KSPLIT == 2 ? 2 : IPW) * OX * 4 <= KSPLIT * TILE * 2, "O exchange fits the tile buffers");
+    auto xo_slot = [&](int part) -> SQA_LDS float* {
+      if constexpr (KSPLIT == 2)
+        return (SQA_LDS float*)(wave < 2 ? (SQA_LDS uint16_t*)lds_k0 : (SQA_LDS uint16_t*)lds_k1) + (wave & 1) * OX;
+      else
+        return (SQA_LDS float*)(part == 1   ? (SQA_LDS uint16_t*)lds_k0
+                                : part == 2 ? (SQA_LDS uint16_t*)lds_k1
+                                            : (SQA_LDS uint16_t*)lds_v0) + wave * OX;
+    };
+    SQA_LDS float* xm = (SQA_LDS float*)(KSPLIT == 2 ? (SQA_LDS uint16_t*)lds_v0 : (SQA_LDS uint16_t*)lds_v1);
     wait_copies();
     __syncthreads();
-    SQA_LDS float* xo = (SQA_LDS float*)(wave < 2 ? (SQA_LDS uint16_t*)lds_k0 : (SQA_LDS uint16_t*)lds_k1) +
-                        (wave & 1) * DB * 16 * 64;
-    SQA_LDS float* xm = (SQA_LDS float*)lds_v0;   // [IPW][2][64]
-    if (kpart == 1 && active) {
+    if (kpart > 0 && active) {
+      SQA_LDS float* xo = xo_slot(kpart);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) xo[(db * 16 + r) * 64 + lane] = o[db][r];
-      xm[(wave * 2) * 64 + lane] = m_run;
-      xm[(wave * 2 + 1) * 64 + lane] = l_run;
+      xm[(((kpart - 1) * IPW + wave) * 2) * 64 + lane] = m_run;
+      xm[(((kpart - 1) * IPW + wave) * 2 + 1) * 64 + lane] = l_run;
     }
     __syncthreads();
-    if (kpart == 1) return;
+    if (kpart > 0) return;
     if (active) {
-      const float m1 = xm[(wave * 2) * 64 + lane];
-      const float l1 = xm[(wave * 2 + 1) * 64 + lane];
-      const float m_new = fmaxf(m_run, m1);
-      const float a0 = __builtin_amdgcn_exp2f(m_run - m_new);
-      const float a1 = __builtin_amdgcn_exp2f(m1 - m_new);
-      l_run = l_run * a0 + l1 * a1;
+      // one part at a time: rescale to the larger maximum and add
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int j = 0; j < KSPLIT - 1; ++j) {
+        const float mj = xm[((j * IPW + wave) * 2) * 64 + lane];
+        const float lj = xm[((j * IPW + wave) * 2 + 1) * 64 + lane];
+        const SQA_LDS float* xo = xo_slot(j + 1);
+        const float m_new = fmaxf(m_run, mj);
+        const float a0 = __builtin_amdgcn_exp2f(m_run - m_new);
+        const float a1 = __builtin_amdgcn_exp2f(mj - m_new);
+        l_run = l_run * a0 + lj * a1;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + xo[(db * 16 + r) * 64 + lane] * a1;
-      m_run = m_new;
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + xo[(db * 16 + r) * 64 + lane] * a1;
+          // each part's reads stay after the previous part's sums (hoisted
+          // together they spilled)
+          asm volatile("" : "+v"(o[db]));
+        }
+        m_run = m_new;
+      }
     }
   }
 
@@ -487,9 +508,14 @@ constexpr int kCUs = 256;
 // - d = 64: 8 waves, 64-key tiles, held to 128 VGPRs so that two workgroups
 //   share a CU (4 waves per SIMD); taken from 512 workgroups on.  Measured
 //   1.5-7 % faster than 128-key tiles at 2 waves per SIMD.  Non-causal
-//   grids of 128-511 such workgroups split the key range in two (twice the
-//   workgroups): at S = 4096, B = 2, the 4/4 heads went from 0.0544 to
-//   0.0430 ms and the 8/4 heads from 0.0789 to 0.0764 ms.
+//   grids of 129-511 such workgroups split the key range in two (twice the
+//   workgroups): at S = 4096, B = 2, the 8/4 heads went from 0.0789 to
+//   0.0764 ms.  Smaller non-causal grids split it in four, with 16-wave
+//   workgroups (four items, 128 KiB of LDS, one per CU at 4 waves per
+//   SIMD).  The 4/4 heads at S = 4096, B = 2 (128 such workgroups): 0.0544
+//   ms unsplit, 0.0430 ms split in two (one box); on another box 0.0422 ms
+//   split in two, 0.0400 ms split in four, and 0.0406 ms split in two with
+//   a third tile buffer (LDS allows it at one workgroup per CU).
 // - d = 32: 8 waves, 128-key tiles (126 VGPRs, two workgroups per CU); taken
 //   from 512 workgroups on.  2-5 % faster than the 4-wave shape.
 template <int D, bool CAUSAL>
@@ -499,7 +525,8 @@ hipError_t launch_bf16_t(const LaunchArgs& a) {
   if constexpr (D == 64) {
     if (wgs8 >= 2 * kCUs) return launch_bf16_w<D, CAUSAL, 8, 64>(a);
     if constexpr (!CAUSAL) {
-      if (wgs8 * 2 >= kCUs) return launch_bf16_w<D, CAUSAL, 8, 64, 2>(a);
+      if (wgs8 * 2 > kCUs) return launch_bf16_w<D, CAUSAL, 8, 64, 2>(a);
+      return launch_bf16_w<D, CAUSAL, 16, 64, 4>(a);
     }
   } else {
     if (wgs8 >= 2 * kCUs) return launch_bf16_w<D, CAUSAL, 8, 128>(a);

@@ -216,14 +216,19 @@ def test_lse_full_size_sampled(name, variant):
     _check_lse(got, oracle.lse(q, k, float(np.float32(w.scale)), causal=w.causal, rows=rows), "bf16", name)
 
 
-# Non-causal d = 64 grids of 128-511 eight-wave workgroups, where every
-# workgroup splits its key range in two and merges the halves: an odd tile
-# count with a 32-key last tile, a 4-key last tile with two heads per group,
-# one tile per workgroup (the second half has no keys), two tiles with a
-# partial second one, the S = 4096 4/4 shape whole, and four heads per group.
+# Non-causal d = 64 grids too small for two eight-wave workgroups per CU
+# split each workgroup's key range and merge the parts.  129-511 such
+# workgroups: two parts per item (8-wave workgroups) -- a 4-key last tile
+# with two heads per group, four heads per group, the S = 4096 8/4 shape
+# whole, and an odd tile count with a 32-key last tile.  At most 128: four
+# parts (16-wave workgroups) -- 63 tiles with a 32-key last one, one tile
+# (parts 1-3 empty), two tiles with a partial second one (parts 2-3 empty),
+# the S = 4096 4/4 shape whole, five tiles over two heads per group (part 3
+# empty), and a single key.
 KEY_SPLIT = [
-    (1, 4000, 8, 8, 64), (2, 2500, 8, 4, 64), (16, 64, 8, 8, 64), (32, 100, 4, 4, 64),
-    (2, 4096, 4, 4, 64), (2, 3000, 16, 4, 64),
+    (2, 2500, 8, 4, 64), (2, 3000, 16, 4, 64), (2, 4096, 8, 4, 64), (1, 4000, 16, 16, 64),
+    (1, 4000, 8, 8, 64), (16, 64, 8, 8, 64), (32, 100, 4, 4, 64), (2, 4096, 4, 4, 64), (1, 300, 2, 1, 64),
+    (1, 1, 4, 4, 64),
 ]
 
 
@@ -244,11 +249,13 @@ def test_key_split_full_output_and_lse(B, S, H_q, H_kv, d):
         _say(f"  scale={scale} {st}")
 
 
-def test_key_split_peaked_second_half():
+@pytest.mark.parametrize("B", [16, 32])
+def test_key_split_peaked_second_half(B):
     """The largest scores sit in the second half of the keys (positions
-    scaled by 8 there), so the merge must rescale the first half's sums by
-    a large factor."""
-    B, S, H_q, H_kv, d = 16, 256, 8, 8, 64
+    scaled by 8 there), so the merge must rescale the first parts' sums by
+    a large factor.  B = 16 gives 128 workgroups (four parts of one tile
+    each), B = 32 gives 256 (two parts of two tiles)."""
+    S, H_q, H_kv, d = 256, 8, 8, 64
     q = inputs.normal(4501, 0, (B, S, H_q, d), "bf16", 0.5)
     k = inputs.normal(4501, 1, (B, S, H_kv, d), "bf16", 0.5)
     v = inputs.normal(4501, 2, (B, S, H_kv, d), "bf16", 0.5)
