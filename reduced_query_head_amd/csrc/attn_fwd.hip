@@ -426,49 +426,188 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
     }
 }
 
-// fp32 path: one thread per (b, position, head), online softmax over keys in
-// fp32.  Plain VALU arithmetic; meant for exactness checks at small sizes.
-template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_f32(const float* __restrict__ q,
-                                                    const float* __restrict__ k,
-                                                    const float* __restrict__ v, float* __restrict__ o,
-                                                    float* __restrict__ lse, int64_t B, int S, int H_q,
-                                                    int H_kv, int R, float c, int causal) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= B * S * H_q) return;
-  const int h = (int)(t % H_q);
-  const int i = (int)((t / H_q) % S);
-  const int64_t b = t / ((int64_t)H_q * S);
-  const int g = h / R;
-  float qv[D], acc[D];
-  const float* qp = q + t * D;
+struct F32Params {
+  const float* q;
+  const float* k;
+  const float* v;
+  float* o;
+  float* lse;            // optional [B, S, H_q] row log-normaliser (natural log)
+  int S;
+  int H_q;
+  int H_kv;
+  int R;
+  int n_groups;          // B * H_kv
+  int n_items;           // R * ceil(S / 32), items per group
+  int chunks;            // ceil(n_items / 4), workgroups per group
+  float c;               // |scale| * log2(e), strictly positive
+  uint32_t q_sign;       // 0x80000000 when scale < 0: q is negated on load (exact)
+  int64_t q_stride;      // elements between consecutive positions of q
+  int64_t kv_stride;     // same for k and v
+};
+
+// fp32 path on the matrix cores: v_mfma_f32_32x32x2_f32 (fp32 operands and
+// accumulation) for both products, the same transposed formulation as the
+// bf16 kernel (S^T = K Q^T with keys along M; O^T += V^T P^T with the score
+// accumulator as the P operand, in fp32).  A workgroup of 4 waves owns one
+// K/V group and 4 items of 32 query positions (position-major, head-minor);
+// 32-key K and V tiles are staged in LDS through registers with rows padded
+// by one float (the K operand reads a column: 32 rows at one dim), double
+// buffered with the next-but-one tile's loads in flight.  Each wave holds its
+// Q^T operand (D/2 floats per lane) for the whole key loop.  The softmax is
+// the bf16 kernel's (exp2 domain, lazily moved running maximum), with the
+// probabilities kept in fp32.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void attn_fwd_f32(F32Params p) {
+  constexpr int WAVES = 4;
+  constexpr int KP = D / 2;   // MFMA k-steps over the head dimension (two dims each)
+  constexpr int DB = D / 32;  // 32-row blocks of O^T
+  constexpr int KB = 32;      // keys per tile
+  constexpr int LD = D + 1;   // LDS row stride in floats
+  constexpr int F4 = KB * D / 4 / (WAVES * 64);  // 16-byte copies per thread and matrix
+  static_assert(F4 >= 1 && (KB * D / 4) % (WAVES * 64) == 0, "tile copies must split evenly");
+  __shared__ float lds_k[2][KB * LD];
+  __shared__ float lds_v[2][KB * LD];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int S = p.S;
+
+  // workgroup -> (group, chunk) as in the bf16 kernel; causal heaviest first
+  const int grp = blockIdx.x % p.n_groups;
+  const int ord = blockIdx.x / p.n_groups;
+  const int chunk = CAUSAL ? (p.chunks - 1 - ord) : ord;
+  const int b = grp / p.H_kv;
+  const int g = grp % p.H_kv;
+  const int item = chunk * WAVES + wave;
+  const bool active = item < p.n_items;
+  const int pos0 = (item / p.R) * 32;
+  const int h = g * p.R + item % p.R;
+  const int last_item = min(chunk * WAVES + WAVES - 1, p.n_items - 1);
+  const int wg_last_pos = min((last_item / p.R) * 32 + 31, S - 1);
+  const int n_tiles = CAUSAL ? wg_last_pos / KB + 1 : (S + KB - 1) / KB;
+
+  // tile copies: thread tid moves 16-byte chunks j * 256 + tid of the tile
+  // (row = chunk / (D/4)); key rows past S are clamped (masked in the scores)
+  const float* k_base = p.k + (int64_t)b * S * p.kv_stride + g * D;
+  const float* v_base = p.v + (int64_t)b * S * p.kv_stride + g * D;
+  f32x4 rk[F4], rv[F4];
+  auto load = [&](int t) {
 #pragma unroll
-  for (int e = 0; e < D; ++e) {
-    qv[e] = qp[e];
-    acc[e] = 0.f;
+    for (int j = 0; j < F4; ++j) {
+      const int idx = j * WAVES * 64 + tid;
+      const int row = idx / (D / 4);
+      const int64_t off = (int64_t)min(t * KB + row, S - 1) * p.kv_stride + 4 * (idx % (D / 4));
+      rk[j] = *(const f32x4*)(k_base + off);
+      rv[j] = *(const f32x4*)(v_base + off);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < F4; ++j) {
+      const int idx = j * WAVES * 64 + tid;
+      const int o = (idx / (D / 4)) * LD + 4 * (idx % (D / 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lds_k[buf][o + e] = rk[j][e];
+        lds_v[buf][o + e] = rv[j][e];
+      }
+    }
+  };
+  load(0);
+
+  // Q^T as the B operand: lane holds query pos0 + col, dims 2*ks + half
+  float qf[KP];
+  {
+    const int qrow = min(pos0 + col, S - 1);
+    const float* qp = p.q + ((int64_t)b * S + qrow) * p.q_stride + h * D + half;
+#pragma unroll
+    for (int ks = 0; ks < KP; ++ks) qf[ks] = __uint_as_float(__float_as_uint(qp[2 * ks]) ^ p.q_sign);
   }
-  float m = -__builtin_inff(), l = 0.f;
-  const int last = causal ? i : S - 1;
-  for (int j = 0; j <= last; ++j) {
-    const float* kp = k + ((b * S + j) * H_kv + g) * D;
-    const float* vp = v + ((b * S + j) * H_kv + g) * D;
-    float dot = 0.f;
+
+  f32x16 o[DB];
 #pragma unroll
-    for (int e = 0; e < D; ++e) dot = __builtin_fmaf(qv[e], kp[e], dot);
-    const float x = dot * c;
-    const float m_new = fmaxf(m, x);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    const float pj = __builtin_amdgcn_exp2f(x - m_new);
-    m = m_new;
-    l = l * alpha + pj;
+  for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;
+  const float c = p.c;
+  const int my_q = pos0 + col;
+  const int wave_last = pos0 + 31;
+
+  store(0);
+  if (n_tiles > 1) load(1);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    __syncthreads();   // tile t stored by everyone; tile t-1 fully consumed
+    if (t + 1 < n_tiles) store(buf ^ 1);
+    if (t + 2 < n_tiles) load(t + 2);
+    const int kv0 = t * KB;
+    if (!active || (CAUSAL && kv0 > wave_last)) continue;
+    const float* kt = lds_k[buf];
+    const float* vt = lds_v[buf];
+
+    // S^T = K Q^T: A operand K[key col][dim 2*ks + half]
+    f32x16 s = (f32x16){};
 #pragma unroll
-    for (int e = 0; e < D; ++e) acc[e] = __builtin_fmaf(pj, vp[e], acc[e] * alpha);
+    for (int ks = 0; ks < KP; ++ks)
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(kt[col * LD + 2 * ks + half], qf[ks], s, 0, 0, 0);
+
+    // mask: s[r] holds key kv0 + 8*(r/4) + 4*half + r%4
+    if ((kv0 + KB > S) || (CAUSAL && kv0 + KB - 1 > pos0)) {
+      const int lim = (CAUSAL ? min(my_q, S - 1) : S - 1) - kv0 - 4 * half;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) > lim) s[r] = -__builtin_inff();
+    }
+
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = wave_pair_max(mx);
+    const float m_cand = mx * c;
+    const bool grow = m_cand > m_run + kLazyLog2;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? m_cand : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    }
+    const float neg_m = -m_run;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, neg_m));
+      l_run += s[r];
+    }
+
+    // O^T += V^T P^T: score register r supplies the key pair
+    // 8*(r/4) + r%4 (k = 0, lanes 0-31) and that + 4 (k = 1, lanes 32-63)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * half + (r & 3);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vt[key * LD + db * 32 + col], s[r], o[db], 0, 0, 0);
+    }
   }
-  const float inv = 1.0f / l;
-  if (lse) lse[t] = (m + log2f(l)) * 0.69314718055994531f;
-  float* op = o + t * D;
+
+  if (!active) return;
+  const int out_pos = pos0 + col;
+  if (out_pos >= S) return;  // lanes l and l^32 share out_pos, so pairs leave together
+  const float l_tot = wave_pair_sum(l_run);
+  const float inv = 1.0f / l_tot;
+  if (p.lse && half == 0) p.lse[((int64_t)b * S + out_pos) * p.H_q + h] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
+  float* op = p.o + (((int64_t)b * S + out_pos) * p.H_q + h) * D;
+  // O^T[db] register r holds head dim db*32 + 8*(r/4) + 4*half + r%4
 #pragma unroll
-  for (int e = 0; e < D; ++e) op[e] = acc[e] * inv;
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *(f32x4*)(op + db * 32 + 8 * j + 4 * half) =
+          (f32x4){o[db][4 * j] * inv, o[db][4 * j + 1] * inv, o[db][4 * j + 2] * inv, o[db][4 * j + 3] * inv};
 }
 
 
@@ -534,15 +673,27 @@ hipError_t launch_bf16_t(const LaunchArgs& a) {
   return launch_bf16_w<D, CAUSAL, 4, 64>(a);
 }
 
-template <int D>
+template <int D, bool CAUSAL>
 hipError_t launch_f32_t(const LaunchArgs& a) {
-  const int64_t threads = a.B * a.S * a.H_q;
-  const int64_t blocks = (threads + 255) / 256;
-  // fp32 kernel keeps the sign of scale in c (no bf16 operand to negate)
-  const float c = a.negate_q ? -a.c : a.c;
-  hipLaunchKernelGGL((attn_fwd_f32<D>), dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)a.stream,
-                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out, a.lse, a.B,
-                     (int)a.S, a.H_q, a.H_kv, a.H_q / a.H_kv, c, a.causal);
+  F32Params p;
+  p.q = (const float*)a.q;
+  p.k = (const float*)a.k;
+  p.v = (const float*)a.v;
+  p.o = (float*)a.out;
+  p.lse = a.lse;
+  p.S = (int)a.S;
+  p.H_q = a.H_q;
+  p.H_kv = a.H_kv;
+  p.R = a.H_q / a.H_kv;
+  p.n_groups = (int)(a.B * a.H_kv);
+  p.n_items = p.R * (int)((a.S + 31) / 32);
+  p.chunks = (p.n_items + 3) / 4;
+  p.c = a.c;
+  p.q_sign = a.negate_q ? 0x80000000u : 0u;
+  p.q_stride = a.q_stride;
+  p.kv_stride = a.kv_stride;
+  const int64_t grid = (int64_t)p.n_groups * p.chunks;
+  hipLaunchKernelGGL((attn_fwd_f32<D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0, (hipStream_t)a.stream, p);
   return hipGetLastError();
 }
 
@@ -557,9 +708,9 @@ hipError_t launch_attn_fwd(const LaunchArgs& a) {
     }
   } else {
     switch (a.d) {
-      case 32: return launch_f32_t<32>(a);
-      case 64: return launch_f32_t<64>(a);
-      case 128: return launch_f32_t<128>(a);
+      case 32: return a.causal ? launch_f32_t<32, true>(a) : launch_f32_t<32, false>(a);
+      case 64: return a.causal ? launch_f32_t<64, true>(a) : launch_f32_t<64, false>(a);
+      case 128: return a.causal ? launch_f32_t<128, true>(a) : launch_f32_t<128, false>(a);
     }
   }
   return hipErrorInvalidValue;

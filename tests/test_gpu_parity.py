@@ -110,6 +110,37 @@ def test_f32_other_head_dims(d):
         check(got, ref, "f32", f"f32 d={d} causal={causal}")
 
 
+# fp32 on the matrix cores (32-key tiles, 4 query items per workgroup):
+# many tiles with two heads per group, a one-key tail, a single position,
+# and 18 items per group (two idle waves in each group's last workgroup).
+F32_SHAPES = [(1, 1000, 8, 2, 64), (2, 33, 4, 4, 128), (1, 1, 2, 1, 32), (3, 97, 2, 2, 128), (1, 545, 5, 5, 32)]
+
+
+@pytest.mark.parametrize("B,S,H_q,H_kv,d", F32_SHAPES)
+def test_f32_tiles_tails_and_late_maximum(B, S, H_q, H_kv, d):
+    """Keys of the second half scaled by 8 move the running maximum late in
+    the key loop (the rescale path); the output against the oracle, causal
+    and not, for a positive and a negative scale.  (The scaled keys give
+    log-normalisers of 10-40, where fp32 rounding of the scores alone
+    exceeds the fp32 LSE bound, which assumes unit-size scores; the fp32
+    LSE is checked on N(0, 1) inputs in test_lse_f32_and_negative_scale.)"""
+    _say(f"f32 B={B} S={S} H={H_q}/{H_kv} d={d}")
+    seed = 7700 + S + d
+    q = inputs.normal(seed, 0, (B, S, H_q, d), "f32")
+    k = inputs.normal(seed, 1, (B, S, H_kv, d), "f32")
+    v = inputs.normal(seed, 2, (B, S, H_kv, d), "f32")
+    k[:, S // 2::7] *= 8.0
+    dq, dk, dv = gpu_util.to_device(q), gpu_util.to_device(k), gpu_util.to_device(v)
+    for causal in (False, True):
+        for scale in (1 / math.sqrt(d), -0.2):
+            o = sqa.attn_fwd(dq, dk, dv, scale=scale, causal=causal)
+            torch.cuda.synchronize()
+            sc = float(np.float32(scale))
+            st = check(gpu_util.to_host_f64(o), oracle.attention(q, k, v, sc, causal=causal), "f32",
+                       f"f32 causal={causal} scale={scale}")
+            _say(f"  causal={causal} scale={scale} {st}")
+
+
 def sample_rows(S, seed, extra=()):
     """Query positions checked at full size: both ends, tile and block
     boundaries and seeded random positions."""
