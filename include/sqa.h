@@ -217,7 +217,7 @@ int64_t sqa_attn_decode_workspace_size(int64_t B, int64_t S_max, int32_t H_q, in
  * result can then differ from sqa_attn_decode's in rounding only (a
  * different split of the same sum).  SQA_ERR_UNSUPPORTED when even one split
  * per head does not fit: bf16 with B * H_q * (d + 2) * 4 >
- * SQA_DECODE_SCRATCH_BYTES (more than 129055 sequence-heads at d = 128).
+ * SQA_DECODE_SCRATCH_BYTES (more than 32263 sequence-heads at d = 128).
  * fp32 inputs use no scratch.
  *
  * Every call on one GPU shares that GPU's array, and the array keeps the last
@@ -226,7 +226,7 @@ int64_t sqa_attn_decode_workspace_size(int64_t B, int64_t S_max, int32_t H_q, in
  * on it and give undefined results.  Calls ordered on one stream are safe.
  * Other errors as for sqa_attn_decode.
  */
-#define SQA_DECODE_SCRATCH_BYTES ((int64_t)64 << 20)
+#define SQA_DECODE_SCRATCH_BYTES ((int64_t)16 << 20)
 sqa_status sqa_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
                                    void* out, float* lse, int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv,
                                    int32_t d, sqa_dtype dtype, float scale, sqa_stream_t stream);

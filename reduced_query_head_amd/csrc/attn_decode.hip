@@ -11,16 +11,20 @@
 //
 // Split-KV design, two kernels:
 //  * attn_decode_split: one wave per (b, K/V group g, block of up to 32 query
-//    heads of the group, key split).  The group's query heads are the 32
-//    columns of S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys along M), so a
-//    cache tile is read once for all R heads that share it.  K comes straight
-//    from HBM into the MFMA's A-operand registers; V goes global -> LDS by
-//    DMA into a wave-private double buffer and is read back transposed
-//    (ds_read_b64_tr_b16) for O^T += V^T P^T, as in the forward.  Waves are
-//    independent (no workgroup barrier).  K is loaded two blocks ahead and V
-//    one block ahead, so each wave keeps about 24 KiB of cache reads in
-//    flight.  Each writes the split's running maximum m (log2 units), row sum
-//    l and unnormalised O^T to a workspace.
+//    heads of the group, key split), four waves per workgroup.  The group's
+//    query heads are the 32 columns of S^T = K Q^T on
+//    v_mfma_f32_32x32x16_bf16 (keys along M), so a cache tile is read once
+//    for all R heads that share it.  K comes straight from HBM into the
+//    MFMA's A-operand registers; V goes global -> LDS by DMA into a
+//    wave-private double buffer and is read back transposed
+//    (ds_read_b64_tr_b16) for O^T += V^T P^T, as in the forward.  The waves
+//    run their key loops independently (no barrier); K is loaded two blocks
+//    ahead and V one block ahead, so each wave keeps about 24 KiB of cache
+//    reads in flight.  Each split's running maximum m (log2 units), row sum
+//    l and unnormalised O^T go to a workspace.  With fewer than four K/V
+//    heads the four waves of a workgroup instead share one split, a quarter
+//    of its keys each, and merge their results through LDS before writing
+//    one partial result (a quarter of the partial traffic for MQA).
 //  * attn_decode_combine: one workgroup per (b, h, 32 head dims) merges the
 //    splits of that head: M = max m_s, L = sum l_s 2^(m_s - M),
 //    O = sum O_s 2^(m_s - M) / L, and writes the bf16 output and
@@ -43,7 +47,7 @@ namespace {
 using namespace dev;
 
 constexpr int kBlk = kDecodeBlk;  // keys per block (one S^T MFMA tile)
-constexpr int kWavesDec = 4;      // waves per workgroup (independent)
+constexpr int kWavesDec = kDecodeWaves;   // waves per workgroup (one split)
 constexpr float kLazyLog2D = 8.0f;
 
 struct DecodeParams {
@@ -55,7 +59,6 @@ struct DecodeParams {
   float* part_ml;           // [B, H_q, n_splits, 2]
   uint16_t* out;            // [B, H_q, D]
   float* lse;               // [B, H_q] or null
-  int64_t n_waves;          // B * H_kv * HB * n_splits
   int S_max;
   int H_q;
   int H_kv;
@@ -65,6 +68,7 @@ struct DecodeParams {
   int split_len;            // keys per split, multiple of kBlk
   float c;                  // |scale| * log2(e), > 0
   uint32_t q_sign;          // 0x8000 when scale < 0 (q negated on load, exact)
+  int64_t n_waves;          // independent waves: B * H_kv * HB * n_splits
 };
 
 __device__ __forceinline__ int cache_len(const DecodeParams& p, int b) {
@@ -72,7 +76,7 @@ __device__ __forceinline__ int cache_len(const DecodeParams& p, int b) {
   return min(len, p.S_max);
 }
 
-template <int D>
+template <int D, bool COOP>
 __global__ __launch_bounds__(kWavesDec * 64, 2) void attn_decode_split_bf16(DecodeParams p) {
   constexpr int KS = D / 16;   // MFMA k-steps over the head dimension
   constexpr int DB = D / 32;   // 32-dim blocks of O^T
@@ -83,22 +87,32 @@ __global__ __launch_bounds__(kWavesDec * 64, 2) void attn_decode_split_bf16(Deco
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  // wave -> (b, split, head block, K/V head), K/V head fastest: waves that
-  // run together read all heads of the same cache positions (whole rows)
-  const int64_t wid = (int64_t)blockIdx.x * kWavesDec + wave;
-  if (wid >= p.n_waves) return;   // wave-uniform; no barrier in this kernel
-  const int g = (int)(wid % p.H_kv);
-  const int64_t r1 = wid / p.H_kv;
+  // unit (b, split, head block, K/V head), K/V head fastest, so that units
+  // that run together read all heads of the same cache positions (whole
+  // rows).  Independent waves: one unit per wave.  COOP (fewer than four K/V
+  // heads, where neighbouring units are other splits anyway): one unit per
+  // workgroup, whose four waves take consecutive quarters of the split's
+  // 32-key blocks and merge their partial results at the end, so that one
+  // partial result covers four waves' keys.
+  const int64_t uid = COOP ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * kWavesDec + wave;
+  if (!COOP && uid >= p.n_waves) return;   // wave-uniform; no barrier on this path
+  const int g = (int)(uid % p.H_kv);
+  const int64_t r1 = uid / p.H_kv;
   const int hb = (int)(r1 % p.HB);
   const int64_t r2 = r1 / p.HB;
   const int split = (int)(r2 % p.n_splits);
   const int b = (int)(r2 / p.n_splits);
 
   const int len = cache_len(p, b);
-  const int k0 = split * p.split_len;
-  if (k0 >= len) return;          // empty split: the combine step skips it
-  const int k1 = min(k0 + p.split_len, len);
-  const int n_blk = (k1 - k0 + kBlk - 1) / kBlk;
+  const int ks0 = split * p.split_len;
+  if (ks0 >= len) return;         // empty split (uniform per unit): the combine step skips it
+  const int ks1 = min(ks0 + p.split_len, len);
+  // this wave's keys [k0, k1): the whole split, or its quarter (COOP; 0
+  // blocks for an empty quarter of waves 1-3)
+  const int q_blk = COOP ? ((ks1 - ks0 + kBlk - 1) / kBlk + kWavesDec - 1) / kWavesDec : 0;
+  const int k0 = COOP ? ks0 + wave * q_blk * kBlk : ks0;
+  const int k1 = COOP ? min(k0 + q_blk * kBlk, ks1) : ks1;
+  const int n_blk = k1 > k0 ? (k1 - k0 + kBlk - 1) / kBlk : 0;
 
   const int hc = hb * 32 + col;   // query head of this lane's column, within the group
   const bool valid = hc < p.R;
@@ -108,6 +122,13 @@ __global__ __launch_bounds__(kWavesDec * 64, 2) void attn_decode_split_bf16(Deco
   const uint16_t* k_base = p.k + ((int64_t)b * p.S_max * p.H_kv + g) * D;
   const uint16_t* v_base = p.v + ((int64_t)b * p.S_max * p.H_kv + g) * D;
 
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;
+
+  if (n_blk > 0) {
   TileCopy<D, 1, kBlk> cp;
   cp.init(kv_stride, 0, lane);
   SQA_LDS uint16_t* vbuf0 = (SQA_LDS uint16_t*)lds_v[wave][0];
@@ -154,11 +175,6 @@ __global__ __launch_bounds__(kWavesDec * 64, 2) void attn_decode_split_bf16(Deco
       for (int j = 0; j < 2; ++j) v_off[db][j] = tile_off<D>(4 * half + 8 * j + e, db * 32 + (grp16 & 1) * 16 + 4 * c4);
   }
 
-  f32x16 o[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
   const float c = p.c;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -229,6 +245,44 @@ __global__ __launch_bounds__(kWavesDec * 64, 2) void attn_decode_split_bf16(Deco
     if (t + 1 < n_blk) step(t + 1, kfb, vbuf1, vbuf0);
   }
   wait_copies();   // no load outlives the loop
+  }
+
+  if constexpr (COOP) {
+  // waves 1-3 hand their running maxima, row sums and O^T to wave 0 through
+  // LDS (O^T in their own, now idle, V buffers); wave 0 rescales each to the
+  // larger maximum and adds it (an empty quarter holds m = -inf, l = 0,
+  // O = 0 and adds nothing; wave 0 always has keys)
+  static_assert(DB * 16 * 64 * 4 <= 2 * kBlk * D * 2, "O^T fits a wave's two V buffers");
+  __shared__ float red_ml[kWavesDec][2][64];
+  if (wave > 0) {
+    SQA_LDS float* xo = (SQA_LDS float*)lds_v[wave][0];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[(db * 16 + r) * 64 + lane] = o[db][r];
+    red_ml[wave][0][lane] = m_run;
+    red_ml[wave][1][lane] = l_run;
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 1; w < kWavesDec; ++w) {
+    const SQA_LDS float* xo = (const SQA_LDS float*)lds_v[w][0];
+    const float mw = red_ml[w][0][lane];
+    const float m_new = fmaxf(m_run, mw);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float a1 = __builtin_amdgcn_exp2f(mw - m_new);
+    l_run = l_run * a0 + red_ml[w][1][lane] * a1;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + xo[(db * 16 + r) * 64 + lane] * a1;
+      // keeps each wave's reads after the previous wave's sums
+      asm volatile("" : "+v"(o[db]));
+    }
+    m_run = m_new;
+  }
+  }
 
   const float l_tot = wave_pair_sum(l_run);
   if (!valid) return;
@@ -396,12 +450,15 @@ hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& plan) {
   p.HB = plan.head_blocks;
   p.n_splits = plan.n_splits;
   p.split_len = plan.split_len;
-  p.n_waves = a.B * a.H_kv * plan.head_blocks * plan.n_splits;
   p.c = a.c;
   p.q_sign = a.negate_q ? 0x8000u : 0u;
-  const int64_t wgs = (p.n_waves + kWavesDec - 1) / kWavesDec;
-  hipLaunchKernelGGL((attn_decode_split_bf16<D>), dim3((unsigned)wgs), dim3(kWavesDec * 64), 0,
-                     (hipStream_t)a.stream, p);
+  p.n_waves = a.B * a.H_kv * plan.head_blocks * plan.n_splits;
+  if (plan.coop)
+    hipLaunchKernelGGL((attn_decode_split_bf16<D, true>), dim3((unsigned)plan.n_wgs), dim3(kWavesDec * 64), 0,
+                       (hipStream_t)a.stream, p);
+  else
+    hipLaunchKernelGGL((attn_decode_split_bf16<D, false>), dim3((unsigned)plan.n_wgs), dim3(kWavesDec * 64), 0,
+                       (hipStream_t)a.stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = a.B * a.H_q;

@@ -13,6 +13,7 @@ constexpr int kBwdRows = 32;      // query rows (dq) or keys (dk/dv) per backwar
 constexpr int kBwdWaves = 4;      // waves of a dq workgroup (a dk/dv workgroup has twice as many)
 constexpr int kDkdvChunk = 32;    // key blocks of one group an XCD takes in a row (long sequences)
 constexpr int kDecodeBlk = 32;    // keys per decode block (one S^T MFMA tile)
+constexpr int kDecodeWaves = 4;   // waves per decode split (one workgroup)
 constexpr int64_t kLayerGemmWorkspace = (int64_t)32 << 20;   // bytes offered to the GEMM library
 
 // rows padded to the backward's 64-row tiles
@@ -93,8 +94,9 @@ struct DecodeArgs {
 struct DecodePlan {
   int head_blocks;        // ceil(R / 32)
   int n_splits;
-  int split_len;          // keys per split
-  int64_t n_waves;
+  int split_len;          // keys per split (a multiple of kDecodeBlk)
+  bool coop;              // the waves of a workgroup share one split (H_kv < kDecodeWaves)
+  int64_t n_wgs;          // split workgroups
   int64_t part_o_bytes;
   int64_t workspace_bytes;
 };
@@ -106,7 +108,7 @@ DecodePlan decode_plan(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int3
 hipError_t launch_attn_decode(const DecodeArgs& a);
 
 // Bytes of the library's own fixed decode scratch (one array per GPU).
-constexpr int64_t kDecodeScratchBytes = (int64_t)64 << 20;
+constexpr int64_t kDecodeScratchBytes = (int64_t)16 << 20;
 // Decode with a.workspace ignored: the partial results go to that scratch
 // array of the stream's GPU; splits are planned to fit it.
 hipError_t launch_attn_decode_noalloc(const DecodeArgs& a);

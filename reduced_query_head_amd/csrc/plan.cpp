@@ -43,15 +43,20 @@ int64_t bwd_grid_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv) {
   return a > b ? (a > c ? a : c) : (b > c ? b : c);
 }
 
-// Split plan: about 8 waves per wave slot of the chip (8 per CU), so that
-// the last round is a small part of the work even when many splits are
-// empty (short caches).  Splits shorter than 512 keys are lengthened
-// towards 512 as long as at least 2 waves per slot remain: short splits
-// spend a larger share of their time starting up and add merge work (512
-// instead of 256 made the 32/8 and 16/8 head configurations of a 4 x 128K
-// cache 1-3 % faster).  Each split has at least 64 keys, and at least 16
-// keys per query head it serves, so the fp32 partial results written per
-// split stay within a few percent of the cache bytes it reads.
+// Split plan, first per wave: about 8 waves per wave slot of the chip (8 per
+// CU), so that the last round is a small part of the work even when many
+// splits are empty (short caches).  Wave ranges shorter than 512 keys are
+// lengthened towards 512 as long as at least 2 waves per slot remain: short
+// ones spend a larger share of their time starting up (512 instead of 256
+// made the 32/8 and 16/8 head configurations of a 4 x 128K cache 1-3 %
+// faster).  Each wave has at least 64 keys, and at least 16 keys per query
+// head it serves, so the fp32 partial results written per split stay a
+// small share of the cache bytes it reads.  With fewer K/V heads than waves
+// per workgroup (coop), a split is the range of kDecodeWaves such waves (one
+// workgroup, merged in LDS): a quarter of the partial results.  With more,
+// each wave is a split of its own and a workgroup's waves read neighbouring
+// heads of the same positions (measured 7-11 % faster there than the
+// cooperative splits, which read one head).
 DecodePlan decode_plan(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d, int64_t max_workspace) {
   DecodePlan pl;
   const int64_t R = H_q / H_kv;
@@ -67,6 +72,8 @@ DecodePlan decode_plan(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int3
   if (len < 64) len = 64;
   if (len < 16 * heads_per_wave) len = 16 * heads_per_wave;
   len = (len + kDecodeBlk - 1) / kDecodeBlk * kDecodeBlk;
+  pl.coop = H_kv < kDecodeWaves;
+  if (pl.coop) len *= kDecodeWaves;   // keys per split
   // a workspace bound: at most max_workspace / (bytes per split of every
   // head) splits, so each split covers at least S_max / that many keys
   const int64_t per_split = B * H_q * (int64_t)(d + 2) * 4;
@@ -82,7 +89,7 @@ DecodePlan decode_plan(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int3
   pl.n_splits = (int)(S_max > 0 ? (S_max + len - 1) / len : 1);
   pl.part_o_bytes = B * H_q * (int64_t)pl.n_splits * d * 4;
   pl.workspace_bytes = pl.part_o_bytes + B * H_q * (int64_t)pl.n_splits * 2 * 4;
-  pl.n_waves = units * pl.n_splits;
+  pl.n_wgs = pl.coop ? units * pl.n_splits : (units * pl.n_splits + kDecodeWaves - 1) / kDecodeWaves;
   return pl;
 }
 

@@ -245,12 +245,12 @@ def test_decode_noalloc_invalid_arguments(kw):
 
 
 def test_decode_noalloc_scratch_limit():
-    # one split per head needs B * H_q * (d + 2) * 4 bytes of the 64 MiB
-    # scratch: 129056 bf16 sequence-heads at d = 128 do not fit (rejected
+    # one split per head needs B * H_q * (d + 2) * 4 bytes of the 16 MiB
+    # scratch: 32264 bf16 sequence-heads at d = 128 do not fit (rejected
     # before any HIP call)
     far = 1 << 40
-    rows_max = (64 << 20) // ((128 + 2) * 4)
-    assert rows_max == 129055
+    rows_max = (16 << 20) // ((128 + 2) * 4)
+    assert rows_max == 32263
     big = dict(q=far, k=2 * far, v=3 * far, seqlens=0, out=4 * far, lse=0, S_max=64, H_q=1, H_kv=1)
     assert _call_dec_noalloc(B=rows_max + 1, **big) == sqa.SQA_ERR_UNSUPPORTED
     assert _call_dec_noalloc(B=0, q=0, k=0, v=0, out=0) == sqa.SQA_OK

@@ -6,7 +6,7 @@ Calls come in a row on one GPU, so the second reads a scratch array that
 still holds the first call's partial results; the second call is smaller
 (fewer sequences, heads and positions).  Where the split plan of the
 allocation-free call equals the workspace call's (its partial results fit
-the 64 MiB scratch) the outputs must be bitwise equal; where the plan had to
+the 16 MiB scratch) the outputs must be bitwise equal; where the plan had to
 take longer splits to fit, the two differ in rounding only and are compared
 with the forward's parity bounds, and both are checked against the fp64
 oracle.
@@ -87,12 +87,12 @@ def test_noalloc_equals_workspace_decode_two_calls():
 
 def test_noalloc_longer_splits_then_smaller_call():
     """Eight 64/1 caches of 128K positions: the workspace call's plan needs
-    more than the 64 MiB scratch, so the allocation-free call takes longer
+    more than the 16 MiB scratch, so the allocation-free call takes longer
     splits (same sum, other rounding).  Then a smaller call reuses the
     scratch."""
     B, S_max, H_q, H_kv, d = 8, 131072, 64, 1, 128
     need = sqa.attn_decode_workspace_size(B, S_max, H_q, H_kv, d)
-    assert need > (64 << 20), need
+    assert need > (16 << 20), need
     lens = [131072, 70000, 1, 0, 513, 4096, 99999, 32]
     _say(f"no-alloc long: B={B} S_max={S_max} H={H_q}/{H_kv} workspace plan {need} bytes")
     q, k, v, ln = _case(8103, B, S_max, H_q, H_kv, d, lens)
