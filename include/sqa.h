@@ -90,14 +90,12 @@ typedef enum {
  * synchronisation on the stream.
  *
  * Speed: bf16 runs on bf16 MFMA kernels (the performance path).  The fp32
- * forward runs on the fp32 matrix cores (v_mfma_f32_32x32x2_f32), at
- * 104-132 TFLOP/s measured at S = 4096-32768 (fp32 matrix peak 157.3).
- * The fp32 backward (sqa_attn_bwd) and decode (sqa_attn_decode) run on
- * plain VALU kernels, one thread per query row (in the backward's dK/dV,
- * per key), each looping over its keys (queries) in fp32; they are meant
- * for exactness checks at small sizes.  Their size limits are the same,
- * but their time grows as S^2 per row, so they become impractically slow
- * beyond a few thousand positions.
+ * forward and backward (sqa_attn_bwd) run on the fp32 matrix cores
+ * (v_mfma_f32_32x32x2_f32): the forward at 104-132 TFLOP/s measured at
+ * S = 4096-32768, the backward at up to 91 TFLOP/s credited at 10*d flops
+ * per pair (fp32 matrix peak 157.3).  The fp32 decode (sqa_attn_decode) is a
+ * plain VALU kernel, one thread per (sequence, query head) looping over the
+ * cache, meant for exactness checks at small sizes.
  */
 sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, void* out, int64_t B,
                         int64_t S, int32_t H_q, int32_t H_kv, int32_t d, sqa_dtype dtype,

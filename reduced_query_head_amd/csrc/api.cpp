@@ -79,11 +79,8 @@ SQA_API sqa_status sqa_attn_fwd_lse(const void* q, const void* k, const void* v,
   if (!row_ok(H_q, d) || !row_ok(H_kv, d)) return SQA_ERR_UNSUPPORTED;
   // kernels index positions with 32-bit integers
   if (S > (int64_t)1 << 30) return SQA_ERR_UNSUPPORTED;
-  if (dtype == SQA_BF16) {
-    if (sqa::bf16_grid_size(B, S, H_q, H_kv) > INT32_MAX) return SQA_ERR_UNSUPPORTED;
-  } else {
-    if ((rows * H_q + 255) / 256 > INT32_MAX) return SQA_ERR_UNSUPPORTED;
-  }
+  // the bf16 and fp32 forward grids have at most fwd_grid_size workgroups
+  if (sqa::fwd_grid_size(B, S, H_q, H_kv) > INT32_MAX) return SQA_ERR_UNSUPPORTED;
 
   sqa::LaunchArgs a;
   a.q = q;
@@ -158,8 +155,11 @@ SQA_API sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, con
   if (d != 32 && d != 64 && d != 128) return SQA_ERR_UNSUPPORTED;
   if (!row_ok(H_q, d) || !row_ok(H_kv, d)) return SQA_ERR_UNSUPPORTED;
   if (S > (int64_t)1 << 30) return SQA_ERR_UNSUPPORTED;
+  // fp32: dq as the forward's grid, dk/dv one workgroup per 128 keys, the
+  // statistics one thread per padded row
   if (dtype == SQA_BF16 ? sqa::bwd_grid_size(B, S, H_q, H_kv) > INT32_MAX
-                        : (rows * H_q + 255) / 256 > INT32_MAX)
+                        : (sqa::fwd_grid_size(B, S, H_q, H_kv) > INT32_MAX ||
+                           (B * H_q * sqa::pad64(S) + 255) / 256 > INT32_MAX))
     return SQA_ERR_UNSUPPORTED;
 
   sqa::BwdArgs a;
@@ -328,7 +328,7 @@ SQA_API sqa_status sqa_layer_fwd(const void* x, const void* w_qkv, const void* w
   if (!row_ok((int64_t)H_q + 2 * (int64_t)H_kv, d)) return SQA_ERR_UNSUPPORTED;
   // rows of x, W_qkv and W_o must stay 16-byte aligned for the GEMM library
   if (d_model % 8 != 0) return SQA_ERR_UNSUPPORTED;
-  if (S > (int64_t)1 << 30 || sqa::bf16_grid_size(B, S, H_q, H_kv) > INT32_MAX) return SQA_ERR_UNSUPPORTED;
+  if (S > (int64_t)1 << 30 || sqa::fwd_grid_size(B, S, H_q, H_kv) > INT32_MAX) return SQA_ERR_UNSUPPORTED;
 
   sqa::LayerArgs a;
   a.x = x;

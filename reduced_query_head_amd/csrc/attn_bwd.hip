@@ -560,7 +560,8 @@ __global__ __launch_bounds__(512, MIN_WAVES_PER_SIMD) void bwd_dkdv_bf16(BwdPara
 }
 
 // ---------------------------------------------------------------------------
-// fp32 path: plain VALU loops in fp32 (small sizes; exactness checks).
+// fp32 path: row statistics as above (plain fp32 loop), then dq and dk/dv on
+// the fp32 matrix cores.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_stats_f32(const float* o, const float* dout, const float* lse, float* ws_lse2,
                                                      float* ws_delta, int64_t B, int S, int S_pad, int H_q) {
@@ -579,81 +580,309 @@ __global__ __launch_bounds__(256) void bwd_stats_f32(const float* o, const float
   ws_lse2[row] = lse[(b * S + i) * H_q + h] * 1.4426950408889634f;
 }
 
+struct F32BwdParams {
+  const float* q;
+  const float* k;
+  const float* v;
+  const float* dout;
+  const float* ws_lse2;   // [B, H_q, S_pad] lse * log2(e)
+  const float* ws_delta;  // [B, H_q, S_pad] D_i = <dO_i, O_i>
+  float* dq;
+  float* dk;
+  float* dv;
+  int S;
+  int S_pad;
+  int H_q;
+  int H_kv;
+  int R;
+  int n_groups;   // B * H_kv
+  int n_items;    // R * ceil(S / 32), query items per group (dq)
+  int chunks;     // ceil(n_items / 4), dq workgroups per group
+  int key_blocks; // ceil(S / 128), dk/dv workgroups per group
+  float c;        // |scale| * log2(e), strictly positive (a tiny value when scale == 0)
+  uint32_t neg;   // 0x80000000 when scale < 0: the S product's register operand is negated
+  float scale;
+};
+
+// Tiles of 32 rows of D floats staged through registers into LDS rows padded
+// by one float (an MFMA operand that reads a column -- 32 rows at one
+// dim -- hits 32 distinct banks).  Thread tid moves 16-byte chunks
+// j * 256 + tid; rows at or past S are clamped to S - 1 (in bounds; their
+// contributions are masked).
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dq_f32(const float* q, const float* k, const float* v, const float* dout,
-                                                  const float* ws_lse2, const float* ws_delta, float* dq, int64_t B,
-                                                  int S, int S_pad, int H_q, int H_kv, int R, float c, float scale,
-                                                  int causal) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (b, i, h)
-  if (t >= B * S * H_q) return;
-  const int h = (int)(t % H_q);
-  const int i = (int)((t / H_q) % S);
-  const int64_t b = t / ((int64_t)H_q * S);
-  const int g = h / R;
-  const int64_t srow = (b * H_q + h) * S_pad + i;
-  const float lse2 = ws_lse2[srow], delta = ws_delta[srow];
-  float acc[D];
+struct F32Tile {
+  static constexpr int LD = D + 1;
+  static constexpr int F4 = 32 * D / 4 / 256;
+  static_assert(F4 >= 1 && (32 * D / 4) % 256 == 0, "tile copies must split evenly");
+  f32x4 r[F4];
+  __device__ __forceinline__ void load(const float* base, int64_t stride, int row0, int S, int tid) {
 #pragma unroll
-  for (int e = 0; e < D; ++e) acc[e] = 0.f;
-  const float* qp = q + t * D;
-  const float* gp = dout + t * D;
-  const int last = causal ? i : S - 1;
-  for (int j = 0; j <= last; ++j) {
-    const float* kp = k + ((b * S + j) * H_kv + g) * D;
-    const float* vp = v + ((b * S + j) * H_kv + g) * D;
-    float s = 0.f, dp = 0.f;
-    for (int e = 0; e < D; ++e) {
-      s = __builtin_fmaf(qp[e], kp[e], s);
-      dp = __builtin_fmaf(gp[e], vp[e], dp);
+    for (int j = 0; j < F4; ++j) {
+      const int idx = j * 256 + tid;
+      r[j] = *(const f32x4*)(base + (int64_t)min(row0 + idx / (D / 4), S - 1) * stride + 4 * (idx % (D / 4)));
     }
-    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s, c, -lse2));
-    const float ds = pv * (dp - delta);
-#pragma unroll
-    for (int e = 0; e < D; ++e) acc[e] = __builtin_fmaf(ds, kp[e], acc[e]);
   }
-  float* op = dq + t * D;
+  __device__ __forceinline__ void store(float* lds, int tid) const {
 #pragma unroll
-  for (int e = 0; e < D; ++e) op[e] = acc[e] * scale;
+    for (int j = 0; j < F4; ++j) {
+      const int idx = j * 256 + tid;
+      const int o = (idx / (D / 4)) * LD + 4 * (idx % (D / 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lds[o + e] = r[j][e];
+    }
+  }
+};
+
+// dq on v_mfma_f32_32x32x2_f32, in the forward fp32 kernel's layout: a
+// workgroup of 4 waves owns one K/V group and 4 items of 32 query rows; K
+// and V tiles of 32 keys pass through LDS.  Per tile and wave,
+// S^T = K Q^T and dP^T = V dO^T (keys along M, this lane's query along N, so
+// lse and D_i are per-lane scalars), P = 2^(c s - lse2), dS = P (dP - D_i),
+// and dQ^T += K^T dS^T with the dS register r as the B operand for the key
+// pair 8*(r/4) + r%4 and + 4 (the two wave halves).  dq = scale * dQ.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dq_f32(F32BwdParams p) {
+  constexpr int WAVES = 4, KP = D / 2, DB = D / 32, KB = 32, LD = F32Tile<D>::LD;
+  __shared__ float lds_k[2][KB * LD];
+  __shared__ float lds_v[2][KB * LD];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int S = p.S;
+  const int grp = blockIdx.x % p.n_groups;
+  const int ord = blockIdx.x / p.n_groups;
+  const int chunk = CAUSAL ? (p.chunks - 1 - ord) : ord;
+  const int b = grp / p.H_kv;
+  const int g = grp % p.H_kv;
+  const int item = chunk * WAVES + wave;
+  const bool active = item < p.n_items;
+  const int pos0 = (item / p.R) * 32;
+  const int h = g * p.R + item % p.R;
+  const int last_item = min(chunk * WAVES + WAVES - 1, p.n_items - 1);
+  const int wg_last_pos = min((last_item / p.R) * 32 + 31, S - 1);
+  const int n_tiles = CAUSAL ? wg_last_pos / KB + 1 : (S + KB - 1) / KB;
+  const int my_q = pos0 + col;
+
+  const int64_t kv_stride = (int64_t)p.H_kv * D;
+  const float* k_base = p.k + (int64_t)b * S * kv_stride + g * D;
+  const float* v_base = p.v + (int64_t)b * S * kv_stride + g * D;
+  F32Tile<D> tk, tv;
+  tk.load(k_base, kv_stride, 0, S, tid);
+  tv.load(v_base, kv_stride, 0, S, tid);
+
+  // this lane's query row: Q^T (negated for a negative scale, so that the
+  // masks' -inf scores stay -inf with c > 0) and dO^T operands (dims
+  // 2*ks + half), lse2 (+inf for rows past S, so that their P is exactly 0)
+  // and D_i
+  float qf[KP], gf[KP];
+  float lse2 = __builtin_inff(), delta = 0.f;
+  {
+    const int qrow = min(my_q, S - 1);
+    const int64_t off = (((int64_t)b * S + qrow) * p.H_q + h) * D + half;
+#pragma unroll
+    for (int ks = 0; ks < KP; ++ks) {
+      qf[ks] = __uint_as_float(__float_as_uint(p.q[off + 2 * ks]) ^ p.neg);
+      gf[ks] = p.dout[off + 2 * ks];
+    }
+    if (active && my_q < S) {
+      const int64_t srow = ((int64_t)b * p.H_q + h) * p.S_pad + my_q;
+      lse2 = p.ws_lse2[srow];
+      delta = p.ws_delta[srow];
+    }
+  }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
+  const float c = p.c;
+  const int wave_last = pos0 + 31;
+
+  tk.store(lds_k[0], tid);
+  tv.store(lds_v[0], tid);
+  if (n_tiles > 1) {
+    tk.load(k_base, kv_stride, KB, S, tid);
+    tv.load(v_base, kv_stride, KB, S, tid);
+  }
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    __syncthreads();   // tile t stored by everyone; tile t-1 fully consumed
+    if (t + 1 < n_tiles) {
+      tk.store(lds_k[buf ^ 1], tid);
+      tv.store(lds_v[buf ^ 1], tid);
+    }
+    if (t + 2 < n_tiles) {
+      tk.load(k_base, kv_stride, (t + 2) * KB, S, tid);
+      tv.load(v_base, kv_stride, (t + 2) * KB, S, tid);
+    }
+    const int kv0 = t * KB;
+    if (!active || (CAUSAL && kv0 > wave_last)) continue;
+    const float* kt = lds_k[buf];
+    const float* vt = lds_v[buf];
+    f32x16 s = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < KP; ++ks) {
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(kt[col * LD + 2 * ks + half], qf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x2f32(vt[col * LD + 2 * ks + half], gf[ks], dp, 0, 0, 0);
+    }
+    // s[r] holds key kv0 + 8*(r/4) + 4*half + r%4
+    if ((kv0 + KB > S) || (CAUSAL && kv0 + KB - 1 > pos0)) {
+      const int lim = (CAUSAL ? min(my_q, S - 1) : S - 1) - kv0 - 4 * half;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) > lim) s[r] = -__builtin_inff();
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2)) * (dp[r] - delta);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * half + (r & 3);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(kt[key * LD + db * 32 + col], s[r], o[db], 0, 0, 0);
+    }
+  }
+
+  if (!active || my_q >= S) return;
+  float* op = p.dq + (((int64_t)b * S + my_q) * p.H_q + h) * D;
+  const float sc = p.scale;
+  // dQ^T[db] register r holds head dim db*32 + 8*(r/4) + 4*half + r%4
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *(f32x4*)(op + db * 32 + 8 * j + 4 * half) =
+          (f32x4){o[db][4 * j] * sc, o[db][4 * j + 1] * sc, o[db][4 * j + 2] * sc, o[db][4 * j + 3] * sc};
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void bwd_dkdv_f32(const float* q, const float* k, const float* v, const float* dout,
-                                                    const float* ws_lse2, const float* ws_delta, float* dk, float* dv,
-                                                    int64_t B, int S, int S_pad, int H_q, int H_kv, int R, float c,
-                                                    float scale, int causal) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (b, j, g)
-  if (t >= B * S * H_kv) return;
-  const int g = (int)(t % H_kv);
-  const int j = (int)((t / H_kv) % S);
-  const int64_t b = t / ((int64_t)H_kv * S);
-  const float* kp = k + t * D;
-  const float* vp = v + t * D;
-  float ak[D], av[D];
+// dk and dv on v_mfma_f32_32x32x2_f32: a workgroup of 4 waves owns 128 keys
+// of one K/V group, each wave 32 of them with their K^T and V^T operands in
+// registers (this lane's key, dims 2*ks + half).  Tiles of 32 query rows of
+// Q and dO, with their lse2 and D_i, stream through LDS for all R query
+// heads of the group, so the sum over the group happens in registers.  Per
+// tile and wave, S = Q K^T and dP = dO V^T (queries along M, this lane's key
+// along N), P = 2^(c s - lse2_i), dS = P (dP - D_i), then dV^T += dO^T P and
+// dK^T += Q^T dS with the register r as the B operand for the query pair
+// 8*(r/4) + r%4 and + 4.  dk = scale * dK.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_f32(F32BwdParams p) {
+  constexpr int KP = D / 2, DB = D / 32, QT = 32, LD = F32Tile<D>::LD;
+  __shared__ float lds_q[2][QT * LD];
+  __shared__ float lds_g[2][QT * LD];
+  __shared__ float lds_st[2][2 * QT];   // [lse2 x 32 | D_i x 32]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const int S = p.S;
+  const int grp = blockIdx.x % p.n_groups;
+  const int kb = blockIdx.x / p.n_groups;
+  const int b = grp / p.H_kv;
+  const int g = grp % p.H_kv;
+  const int key_wg0 = kb * 128;
+  const int wave_key0 = key_wg0 + wave * 32;
+  const int my_key = wave_key0 + col;
+
+  const int qt_first = CAUSAL ? key_wg0 / QT : 0;
+  const int qt_count = (S + QT - 1) / QT - qt_first;
+  const int U = p.R * qt_count;
+
+  const int64_t q_stride = (int64_t)p.H_q * D;
+  F32Tile<D> tq, tg;
+  float st_val = __builtin_inff();
+  auto load = [&](int u) {
+    const int h = g * p.R + u / qt_count;
+    const int row0 = (qt_first + u % qt_count) * QT;
+    const int64_t base = ((int64_t)b * S * p.H_q + h) * D;
+    tq.load(p.q + base, q_stride, row0, S, tid);
+    tg.load(p.dout + base, q_stride, row0, S, tid);
+    if (tid < 2 * QT) {   // lse2 (+inf past S: P = 0) and D_i of the tile's rows
+      const int i = row0 + (tid & (QT - 1));
+      const int64_t srow = ((int64_t)b * p.H_q + h) * p.S_pad + min(i, S - 1);
+      st_val = tid < QT ? (i < S ? p.ws_lse2[srow] : __builtin_inff()) : p.ws_delta[srow];
+    }
+  };
+  auto store = [&](int buf) {
+    tq.store(lds_q[buf], tid);
+    tg.store(lds_g[buf], tid);
+    if (tid < 2 * QT) lds_st[buf][tid] = st_val;
+  };
+
+  // this lane's key: K^T (negated for a negative scale: the S product only;
+  // dK uses Q as given) and V^T operands (rows past S clamped; not stored)
+  float kf[KP], vf[KP];
+  {
+    const int64_t off = (((int64_t)b * S + min(my_key, S - 1)) * p.H_kv + g) * D + half;
 #pragma unroll
-  for (int e = 0; e < D; ++e) ak[e] = av[e] = 0.f;
-  for (int h = g * R; h < (g + 1) * R; ++h)
-    for (int i = causal ? j : 0; i < S; ++i) {
-      const float* qp = q + ((b * S + i) * H_q + h) * D;
-      const float* gp = dout + ((b * S + i) * H_q + h) * D;
-      const int64_t srow = (b * H_q + h) * S_pad + i;
-      float s = 0.f, dp = 0.f;
-      for (int e = 0; e < D; ++e) {
-        s = __builtin_fmaf(qp[e], kp[e], s);
-        dp = __builtin_fmaf(gp[e], vp[e], dp);
-      }
-      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s, c, -ws_lse2[srow]));
-      const float ds = pv * (dp - ws_delta[srow]);
+    for (int ks = 0; ks < KP; ++ks) {
+      kf[ks] = __uint_as_float(__float_as_uint(p.k[off + 2 * ks]) ^ p.neg);
+      vf[ks] = p.v[off + 2 * ks];
+    }
+  }
+  f32x16 dk[DB], dv[DB];
 #pragma unroll
-      for (int e = 0; e < D; ++e) {
-        av[e] = __builtin_fmaf(pv, gp[e], av[e]);
-        ak[e] = __builtin_fmaf(ds, qp[e], ak[e]);
-      }
+  for (int db = 0; db < DB; ++db) dk[db] = dv[db] = (f32x16){};
+  const float c = p.c;
+
+  if (U > 0) {
+    load(0);
+    store(0);
+  }
+  if (U > 1) load(1);
+  for (int u = 0; u < U; ++u) {
+    const int buf = u & 1;
+    __syncthreads();   // tile u stored by everyone; tile u-1 fully consumed
+    if (u + 1 < U) store(buf ^ 1);
+    if (u + 2 < U) load(u + 2);
+    const int qbase = (qt_first + u % qt_count) * QT;
+    // every query of the tile before this wave's keys (causal): no work
+    if (CAUSAL && qbase + QT - 1 < wave_key0) continue;
+    const float* qt = lds_q[buf];
+    const float* gt = lds_g[buf];
+    const float* st = lds_st[buf];
+    f32x16 s = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < KP; ++ks) {
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(qt[col * LD + 2 * ks + half], kf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x2f32(gt[col * LD + 2 * ks + half], vf[ks], dp, 0, 0, 0);
+    }
+    // register r: query qbase + 8*(r/4) + 4*half + r%4
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qi = 8 * (r >> 2) + 4 * half + (r & 3);
+      if (CAUSAL && my_key > qbase + qi) s[r] = -__builtin_inff();
+      s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -st[qi]));
+      ds[r] = s[r] * (dp[r] - st[QT + qi]);
     }
 #pragma unroll
-  for (int e = 0; e < D; ++e) {
-    dk[t * D + e] = ak[e] * scale;
-    dv[t * D + e] = av[e];
+    for (int r = 0; r < 16; ++r) {
+      const int qi = 8 * (r >> 2) + 4 * half + (r & 3);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(gt[qi * LD + db * 32 + col], s[r], dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(qt[qi * LD + db * 32 + col], ds[r], dk[db], 0, 0, 0);
+      }
+    }
   }
+
+  if (my_key >= S) return;
+  const int64_t off = (((int64_t)b * S + my_key) * p.H_kv + g) * D;
+  const float sc = p.scale;
+  // dK^T / dV^T[db] register r holds head dim db*32 + 8*(r/4) + 4*half + r%4
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = db * 32 + 8 * j + 4 * half;
+      *(f32x4*)(p.dk + off + e) =
+          (f32x4){dk[db][4 * j] * sc, dk[db][4 * j + 1] * sc, dk[db][4 * j + 2] * sc, dk[db][4 * j + 3] * sc};
+      *(f32x4*)(p.dv + off + e) = (f32x4){dv[db][4 * j], dv[db][4 * j + 1], dv[db][4 * j + 2], dv[db][4 * j + 3]};
+    }
 }
 
 template <int D, bool CAUSAL>
@@ -702,23 +931,39 @@ hipError_t launch_bwd_bf16_t(const BwdArgs& a) {
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool CAUSAL>
 hipError_t launch_bwd_f32_t(const BwdArgs& a) {
-  const int S_pad = (int)pad64(a.S);
+  F32BwdParams p;
+  p.q = (const float*)a.q;
+  p.k = (const float*)a.k;
+  p.v = (const float*)a.v;
+  p.dout = (const float*)a.dout;
+  p.S = (int)a.S;
+  p.S_pad = (int)pad64(a.S);
+  p.H_q = a.H_q;
+  p.H_kv = a.H_kv;
+  p.R = a.H_q / a.H_kv;
   float* ws_lse2 = (float*)a.workspace;
-  float* ws_delta = ws_lse2 + a.B * a.H_q * (int64_t)S_pad;
+  float* ws_delta = ws_lse2 + a.B * a.H_q * (int64_t)p.S_pad;
+  p.ws_lse2 = ws_lse2;
+  p.ws_delta = ws_delta;
+  p.dq = (float*)a.dq;
+  p.dk = (float*)a.dk;
+  p.dv = (float*)a.dv;
+  p.n_groups = (int)(a.B * a.H_kv);
+  p.n_items = p.R * (int)((a.S + 31) / 32);
+  p.chunks = (p.n_items + 3) / 4;
+  p.key_blocks = (int)((a.S + 127) / 128);
+  p.c = a.c;
+  p.neg = a.negate_q ? 0x80000000u : 0u;
+  p.scale = a.scale;
   hipStream_t st = (hipStream_t)a.stream;
-  const float c = a.negate_q ? -a.c : a.c;
-  const int64_t nst = a.B * a.H_q * (int64_t)S_pad;
+  const int64_t nst = a.B * a.H_q * (int64_t)p.S_pad;
   hipLaunchKernelGGL((bwd_stats_f32<D>), dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, st, (const float*)a.out,
-                     (const float*)a.dout, a.lse, ws_lse2, ws_delta, a.B, (int)a.S, S_pad, a.H_q);
-  const int64_t nq = a.B * a.S * a.H_q, nk = a.B * a.S * a.H_kv;
-  hipLaunchKernelGGL((bwd_dq_f32<D>), dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, st, (const float*)a.q,
-                     (const float*)a.k, (const float*)a.v, (const float*)a.dout, ws_lse2, ws_delta, (float*)a.dq, a.B,
-                     (int)a.S, S_pad, a.H_q, a.H_kv, a.H_q / a.H_kv, c, a.scale, a.causal);
-  hipLaunchKernelGGL((bwd_dkdv_f32<D>), dim3((unsigned)((nk + 255) / 256)), dim3(256), 0, st, (const float*)a.q,
-                     (const float*)a.k, (const float*)a.v, (const float*)a.dout, ws_lse2, ws_delta, (float*)a.dk,
-                     (float*)a.dv, a.B, (int)a.S, S_pad, a.H_q, a.H_kv, a.H_q / a.H_kv, c, a.scale, a.causal);
+                     (const float*)a.dout, a.lse, ws_lse2, ws_delta, a.B, (int)a.S, p.S_pad, a.H_q);
+  hipLaunchKernelGGL((bwd_dq_f32<D, CAUSAL>), dim3((unsigned)((int64_t)p.n_groups * p.chunks)), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((bwd_dkdv_f32<D, CAUSAL>), dim3((unsigned)((int64_t)p.n_groups * p.key_blocks)), dim3(256), 0,
+                     st, p);
   return hipGetLastError();
 }
 
@@ -733,9 +978,9 @@ hipError_t launch_attn_bwd(const BwdArgs& a) {
     }
   } else {
     switch (a.d) {
-      case 32: return launch_bwd_f32_t<32>(a);
-      case 64: return launch_bwd_f32_t<64>(a);
-      case 128: return launch_bwd_f32_t<128>(a);
+      case 32: return a.causal ? launch_bwd_f32_t<32, true>(a) : launch_bwd_f32_t<32, false>(a);
+      case 64: return a.causal ? launch_bwd_f32_t<64, true>(a) : launch_bwd_f32_t<64, false>(a);
+      case 128: return a.causal ? launch_bwd_f32_t<128, true>(a) : launch_bwd_f32_t<128, false>(a);
     }
   }
   return hipErrorInvalidValue;

@@ -70,7 +70,7 @@ int64_t bwd_workspace_bytes(int64_t B, int64_t S, int32_t H_q);
 // dk/dv grid size; *kb_chunk = key blocks per XCD chunk (0: no chunking)
 int64_t dkdv_layout(int64_t n_groups, int64_t key_blocks, int* kb_chunk);
 int64_t bwd_grid_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv);
-int64_t bf16_grid_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv);
+int64_t fwd_grid_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv);
 
 struct DecodeArgs {
   const void* q;          // [B, H_q, d]

@@ -13,7 +13,7 @@ int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 }  // namespace
 
 // Forward grid at its largest shape (4 items per workgroup).
-int64_t bf16_grid_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv) {
+int64_t fwd_grid_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv) {
   const int64_t R = H_q / H_kv;
   const int64_t items = R * ((S + kFwdRows - 1) / kFwdRows);
   return B * H_kv * ((items + 3) / 4);

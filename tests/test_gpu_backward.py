@@ -256,6 +256,34 @@ def test_backward_f32(d):
             _check_grad(gpu_util.to_host_f64(got), ref, "f32", f"f32 {name} d={d} c={causal}", allow[name])
 
 
+# fp32 on the matrix cores: several 128-key dk/dv workgroups and 32-row
+# query tiles over two heads per group, a 257-position sequence (a one-row
+# tail) at d = 128, and eight heads on one K/V head with a 33-position
+# sequence; a positive and a negative scale, causal and not.
+F32_BWD = [(2, 300, 6, 3, 64), (1, 257, 4, 4, 128), (1, 33, 8, 1, 32)]
+
+
+@pytest.mark.parametrize("B,S,H_q,H_kv,d", F32_BWD)
+def test_backward_f32_tiles(B, S, H_q, H_kv, d):
+    _say(f"f32 backward B={B} S={S} H={H_q}/{H_kv} d={d}")
+    seed = 9400 + S + d
+    q = inputs.normal(seed, 0, (B, S, H_q, d), "f32")
+    k = inputs.normal(seed, 1, (B, S, H_kv, d), "f32")
+    v = inputs.normal(seed, 2, (B, S, H_kv, d), "f32")
+    dout = inputs.normal(seed, 5, (B, S, H_q, d), "f32")
+    for causal in (False, True):
+        for scale in (1 / math.sqrt(d), -0.2):
+            gq, gk, gv = _run(q, k, v, dout, scale, causal)
+            sc = float(np.float32(scale))
+            rq, rk, rv = oracle.attention_grad(q, k, v, dout, sc, causal=causal)
+            allow = {"dq": dq_allowance(q, k, v, dout, sc, causal, dtype="f32"),
+                     "dk": dk_allowance(q, k, v, dout, sc, causal, dtype="f32"), "dv": None}
+            for name, got, ref in (("dq", gq, rq), ("dk", gk, rk), ("dv", gv, rv)):
+                st = _check_grad(gpu_util.to_host_f64(got), ref, "f32", f"f32 {name} c={causal} scale={scale:.3g}",
+                                 allow[name])
+                _say(f"  {name} causal={causal} scale={scale:.3g} {st}")
+
+
 def test_backward_grouped_equals_mha_on_repeated_kv():
     """dq equal bit for bit; dk/dv of the grouped call equal the per-head MHA
     gradients summed over each group (to fp32/bf16 rounding)."""
