@@ -1,7 +1,7 @@
 """Seeded random configurations, checked in full against the oracle: group
 sizes 1-8 (odd ones included), head dims 32/64/128, sequence lengths next to
 every tile boundary the kernels use (32, 64 and 128 rows or keys), both mask
-modes and a spread of scales.  The draw is fixed (numpy seed 20261203), so
+modes and a spread of scales, for bf16 and (forward and backward) fp32.  The draw is fixed (numpy seed 20261203), so
 every run checks the same cases; they complement the hand-picked shapes of
 the other parity tests."""
 import math
@@ -48,6 +48,9 @@ def _draw(n, seed):
 FWD = _draw(28, 20261203)
 BWD = _draw(12, 20261204)
 DEC = _draw(12, 20261205)
+F32_FWD = _draw(12, 20261206)
+F32_BWD = _draw(8, 20261207)
+F32_LSE_MAX, F32_LSE_MEAN = 2e-5, 2e-6
 
 
 @pytest.mark.parametrize("B,S,H_q,H_kv,d,causal,scale", FWD)
@@ -83,6 +86,44 @@ def test_random_backward(B, S, H_q, H_kv, d, causal, scale):
     allow = {"dq": dq_allowance(q, k, v, g, sc, causal), "dk": dk_allowance(q, k, v, g, sc, causal), "dv": None}
     for name, got, ref in (("dq", gq, rq), ("dk", gk, rk), ("dv", gv, rv)):
         _check_grad(gpu_util.to_host_f64(got), ref, "bf16", f"random {name}", allow[name])
+
+
+@pytest.mark.parametrize("B,S,H_q,H_kv,d,causal,scale", F32_FWD)
+def test_random_forward_and_lse_f32(B, S, H_q, H_kv, d, causal, scale):
+    """The fp32 matrix-core forward on the same kind of draw."""
+    _say(f"f32 fwd B={B} S={S} H={H_q}/{H_kv} d={d} causal={causal} scale={scale:.4g}")
+    seed = 15000 + S + 7 * H_q + d
+    q = inputs.normal(seed, 0, (B, S, H_q, d), "f32", 0.5)
+    k = inputs.normal(seed, 1, (B, S, H_kv, d), "f32", 0.5)
+    v = inputs.normal(seed, 2, (B, S, H_kv, d), "f32", 0.5)
+    dq, dk, dv = (gpu_util.to_device(a) for a in (q, k, v))
+    o, lse = sqa.attn_fwd(dq, dk, dv, scale=scale, causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    sc = float(np.float32(scale))
+    parity.check(gpu_util.to_host_f64(o), oracle.attention(q, k, v, sc, causal=causal), "f32", "random f32 forward")
+    err = np.abs(lse.double().cpu().numpy() - oracle.lse(q, k, sc, causal=causal))
+    assert err.max() <= F32_LSE_MAX and err.mean() <= F32_LSE_MEAN, f"lse max {err.max()} mean {err.mean()}"
+
+
+@pytest.mark.parametrize("B,S,H_q,H_kv,d,causal,scale", F32_BWD)
+def test_random_backward_f32(B, S, H_q, H_kv, d, causal, scale):
+    """The fp32 matrix-core backward on the same kind of draw."""
+    _say(f"f32 bwd B={B} S={S} H={H_q}/{H_kv} d={d} causal={causal} scale={scale:.4g}")
+    seed = 16000 + S + 7 * H_q + d
+    q = inputs.normal(seed, 0, (B, S, H_q, d), "f32", 0.5)
+    k = inputs.normal(seed, 1, (B, S, H_kv, d), "f32", 0.5)
+    v = inputs.normal(seed, 2, (B, S, H_kv, d), "f32", 0.5)
+    g = inputs.normal(seed, 5, (B, S, H_q, d), "f32", 1.0)
+    dq_, dk_, dv_, dg = (gpu_util.to_device(a) for a in (q, k, v, g))
+    o, lse = sqa.attn_fwd(dq_, dk_, dv_, scale=scale, causal=causal, return_lse=True)
+    gq, gk, gv = sqa.attn_bwd(dq_, dk_, dv_, o, dg, lse, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    sc = float(np.float32(scale))
+    rq, rk, rv = oracle.attention_grad(q, k, v, g, sc, causal=causal)
+    allow = {"dq": dq_allowance(q, k, v, g, sc, causal, dtype="f32"),
+             "dk": dk_allowance(q, k, v, g, sc, causal, dtype="f32"), "dv": None}
+    for name, got, ref in (("dq", gq, rq), ("dk", gk, rk), ("dv", gv, rv)):
+        _check_grad(gpu_util.to_host_f64(got), ref, "f32", f"random f32 {name}", allow[name])
 
 
 @pytest.mark.parametrize("B,S,H_q,H_kv,d,causal,scale", DEC)
