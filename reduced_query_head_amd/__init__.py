@@ -1,5 +1,6 @@
 """Python binding of libsqa: decoupled-head attention on MI355X (forward,
-backward, decode, full layer).
+backward, decode, full layer), and `attention`, the forward and backward
+joined for torch.autograd.
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``lib/libsqa.so`` (sources in ``csrc/``, C-ABI in
@@ -222,6 +223,39 @@ def attn_bwd(q, k, v, out, dout, lse, scale=None, causal=False, stream=None, dq=
     if st != SQA_OK:
         raise SqaError(st, status_string(st))
     return dq, dk, dv
+
+
+_attention_fn = None
+
+
+def attention(q, k, v, scale=None, causal=False):
+    """attn_fwd with autograd: the forward runs sqa_attn_fwd_lse and keeps
+    its output and row log-normaliser; backward() runs sqa_attn_bwd on
+    them.  q, k, v as for attn_fwd (contiguous GPU tensors, one dtype);
+    gradients flow to whichever of them require them.  The upstream
+    gradient is made contiguous (a copy only if it is not)."""
+    global _attention_fn
+    import torch
+
+    if _attention_fn is None:
+        class _Attention(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q_, k_, v_, scale_, causal_):
+                out, lse = attn_fwd(q_, k_, v_, scale=scale_, causal=causal_, return_lse=True)
+                ctx.save_for_backward(q_, k_, v_, out, lse)
+                ctx.scale, ctx.causal = scale_, causal_
+                return out
+
+            @staticmethod
+            def backward(ctx, dout):
+                q_, k_, v_, out, lse = ctx.saved_tensors
+                dq, dk, dv = attn_bwd(q_, k_, v_, out, dout.contiguous(), lse, scale=ctx.scale, causal=ctx.causal)
+                return dq, dk, dv, None, None
+
+        _attention_fn = _Attention
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    return _attention_fn.apply(q, k, v, float(scale), bool(causal))
 
 
 def attn_decode_workspace_size(B, S_max, H_q, H_kv, d):

@@ -340,3 +340,35 @@ def test_backward_full_size(name, variant):
     err = float((dv_sum - g_sum).norm() / g_sum.norm())
     assert err < 2e-2, f"sum_j dv_j vs summed dout: {err}"
     _say(f"  identities ok (dv rel {err:.2e})")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_autograd_attention_matches_attn_bwd_and_oracle(dtype):
+    """sqa.attention under torch.autograd: the gradients equal those of a
+    direct attn_bwd call on the same forward outputs (bit for bit; the same
+    kernels), and the oracle's within the parity bounds."""
+    B, S, H_q, H_kv, d = 1, 200, 4, 2, 64
+    mul = 0.5 if dtype == "bf16" else 1.0
+    q = inputs.normal(95, 0, (B, S, H_q, d), dtype, mul)
+    k = inputs.normal(95, 1, (B, S, H_kv, d), dtype, mul)
+    v = inputs.normal(95, 2, (B, S, H_kv, d), dtype, mul)
+    g = inputs.normal(95, 5, (B, S, H_q, d), dtype, 1.0)
+    scale = 0.11
+    tq, tk, tv, tg = (gpu_util.to_device(a) for a in (q, k, v, g))
+    for t in (tq, tk, tv):
+        t.requires_grad_(True)
+    out = sqa.attention(tq, tk, tv, scale=scale, causal=True)
+    out.backward(tg)
+    torch.cuda.synchronize()
+    with torch.no_grad():
+        o2, lse = sqa.attn_fwd(tq.detach(), tk.detach(), tv.detach(), scale=scale, causal=True, return_lse=True)
+        dq, dk, dv = sqa.attn_bwd(tq.detach(), tk.detach(), tv.detach(), o2, tg, lse, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    for a, b in ((out.detach(), o2), (tq.grad, dq), (tk.grad, dk), (tv.grad, dv)):
+        assert torch.equal(a, b)
+    sc = float(np.float32(scale))
+    rq, rk, rv = oracle.attention_grad(q, k, v, g, sc, causal=True)
+    allow = {"dq": dq_allowance(q, k, v, g, sc, True, dtype=dtype), "dk": dk_allowance(q, k, v, g, sc, True, dtype=dtype),
+             "dv": None}
+    for name, got, ref in (("dq", tq.grad, rq), ("dk", tk.grad, rk), ("dv", tv.grad, rv)):
+        _check_grad(gpu_util.to_host_f64(got), ref, dtype, f"autograd {dtype} {name}", allow[name])
