@@ -184,7 +184,7 @@ def time_decode(sqa, torch, wname, steps, warmup):
     return {"workload": w.name, "B": w.B, "S_max": w.S_max, "d": w.d,
             "cache_lengths": [int(x) for x in decode_lengths(w.seed(w.variants[0].name), w.B, w.S_max,
                                                              w.min_len_frac)], "variants": res,
-            "kernels": "attn_decode_split_bf16 + attn_decode_combine_bf16 (one sqa_attn_decode call)"}
+            "kernels": "attn_decode_split_bf16 + attn_decode_combine (one sqa_attn_decode call)"}
 
 
 def time_layer(sqa, torch, wname, steps, warmup):

@@ -93,9 +93,8 @@ typedef enum {
  * forward and backward (sqa_attn_bwd) run on the fp32 matrix cores
  * (v_mfma_f32_32x32x2_f32): the forward at 104-132 TFLOP/s measured at
  * S = 4096-32768, the backward at up to 91 TFLOP/s credited at 10*d flops
- * per pair (fp32 matrix peak 157.3).  The fp32 decode (sqa_attn_decode) is a
- * plain VALU kernel, one thread per (sequence, query head) looping over the
- * cache, meant for exactness checks at small sizes.
+ * per pair (fp32 matrix peak 157.3); the fp32 decode (sqa_attn_decode) on
+ * the same matrix cores with the bf16 decode's split plan.
  */
 sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, void* out, int64_t B,
                         int64_t S, int32_t H_q, int32_t H_kv, int32_t d, sqa_dtype dtype,
@@ -187,10 +186,9 @@ int64_t sqa_attn_bwd_workspace_size(int64_t B, int64_t S, int32_t H_q);
  * SQA_ERR_INVALID_ARGUMENT as for sqa_attn_fwd (and for a short workspace);
  * SQA_ERR_UNSUPPORTED for d not in {32, 64, 128}, H_q * d or H_kv * d above
  * 2^22, or S_max > 2^30.  B == 0
- * is a successful no-op.  Asynchronous on `stream`.  bf16: a split kernel
- * (bf16 MFMA, fp32 accumulation, probabilities rounded to bf16 for the P.V
- * product) and a combine kernel; fp32: a plain fp32 kernel (one thread per
- * sequence and head, workspace unused) for exactness checks at small sizes.
+ * is a successful no-op.  Asynchronous on `stream`.  A split kernel and a
+ * combine kernel: bf16 MFMA with fp32 accumulation and probabilities rounded
+ * to bf16 for the P.V product, or fp32 MFMA with fp32 probabilities.
  */
 sqa_status sqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
                            void* out, float* lse, void* workspace, int64_t workspace_bytes, int64_t B,
@@ -214,9 +212,8 @@ int64_t sqa_attn_decode_workspace_size(int64_t B, int64_t S_max, int32_t H_q, in
  * B * H_q * n_splits * (d + 2) * 4 bytes <= SQA_DECODE_SCRATCH_BYTES.  The
  * result can then differ from sqa_attn_decode's in rounding only (a
  * different split of the same sum).  SQA_ERR_UNSUPPORTED when even one split
- * per head does not fit: bf16 with B * H_q * (d + 2) * 4 >
- * SQA_DECODE_SCRATCH_BYTES (more than 32263 sequence-heads at d = 128).
- * fp32 inputs use no scratch.
+ * per head does not fit: B * H_q * (d + 2) * 4 > SQA_DECODE_SCRATCH_BYTES
+ * (more than 32263 sequence-heads at d = 128).
  *
  * Every call on one GPU shares that GPU's array, and the array keeps the last
  * call's contents: two calls whose execution overlaps on the same GPU (on

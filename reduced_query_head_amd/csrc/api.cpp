@@ -239,11 +239,11 @@ sqa_status decode_checks(const void* q, const void* k_cache, const void* v_cache
   }
   if (d != 32 && d != 64 && d != 128) return SQA_ERR_UNSUPPORTED;
   if (!row_ok(H_q, d) || !row_ok(H_kv, d)) return SQA_ERR_UNSUPPORTED;
-  // split grid (one workgroup per split), combine grid (d/32 workgroups per row), fp32 grid
-  if (plan.n_wgs > INT32_MAX || B * H_q * (d / 32) > INT32_MAX || (B * H_q + 255) / 256 > INT32_MAX)
+  // split grid (one workgroup per split or per four splits), combine grid (d/32 workgroups per row)
+  if (plan.n_wgs > INT32_MAX || B * H_q * (d / 32) > INT32_MAX)
     return SQA_ERR_UNSUPPORTED;
   // the fixed scratch holds at least one split of every head
-  if (no_alloc && dtype == SQA_BF16 && plan.workspace_bytes > sqa::kDecodeScratchBytes) return SQA_ERR_UNSUPPORTED;
+  if (no_alloc && plan.workspace_bytes > sqa::kDecodeScratchBytes) return SQA_ERR_UNSUPPORTED;
 
   a->q = q;
   a->k = k_cache;

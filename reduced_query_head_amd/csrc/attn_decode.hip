@@ -31,7 +31,8 @@
 //    lse = ln2 (M + log2 L).
 // Cache lengths come from a device array (or are all S_max); a length above
 // S_max counts as S_max, and an empty cache gives out = 0, lse = -inf.
-// fp32 inputs take a plain one-thread-per-(b, h) kernel (exactness checks).
+// fp32 inputs take the same plan and merge with the products on the fp32
+// matrix cores (attn_decode_split_f32) and an fp32 output.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -67,13 +68,52 @@ struct DecodeParams {
   int n_splits;
   int split_len;            // keys per split, multiple of kBlk
   float c;                  // |scale| * log2(e), > 0
-  uint32_t q_sign;          // 0x8000 when scale < 0 (q negated on load, exact)
+  uint32_t q_sign;          // scale < 0: 0x8000 (bf16) or 0x80000000 (fp32), q negated on load (exact)
   int64_t n_waves;          // independent waves: B * H_kv * HB * n_splits
 };
 
 __device__ __forceinline__ int cache_len(const DecodeParams& p, int b) {
   const int len = p.seqlens ? p.seqlens[b] : p.S_max;
   return min(len, p.S_max);
+}
+
+// Merge of a shared split (COOP): waves 1-3 hand their running maxima, row
+// sums and O^T to wave 0 through LDS (xo(w): wave w's O^T slot, DB*16*64
+// floats); wave 0 rescales each to the larger maximum and adds it (an empty
+// quarter holds m = -inf, l = 0, O = 0 and adds nothing; wave 0 always has
+// keys).  Returns true in wave 0, which goes on to write the partial result.
+template <int DB, class XO>
+__device__ __forceinline__ bool coop_merge(f32x16 (&o)[DB], float& m_run, float& l_run, int wave, int lane, XO xo,
+                                           float (*red_ml)[2][64]) {
+  if (wave > 0) {
+    SQA_LDS float* x = xo(wave);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[(db * 16 + r) * 64 + lane] = o[db][r];
+    red_ml[wave][0][lane] = m_run;
+    red_ml[wave][1][lane] = l_run;
+  }
+  __syncthreads();
+  if (wave > 0) return false;
+#pragma unroll
+  for (int w = 1; w < kWavesDec; ++w) {
+    const SQA_LDS float* x = xo(w);
+    const float mw = red_ml[w][0][lane];
+    const float m_new = fmaxf(m_run, mw);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float a1 = __builtin_amdgcn_exp2f(mw - m_new);
+    l_run = l_run * a0 + red_ml[w][1][lane] * a1;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + x[(db * 16 + r) * 64 + lane] * a1;
+      // keeps each wave's reads after the previous wave's sums
+      asm volatile("" : "+v"(o[db]));
+    }
+    m_run = m_new;
+  }
+  return true;
 }
 
 template <int D, bool COOP>
@@ -248,40 +288,166 @@ __global__ __launch_bounds__(kWavesDec * 64, 2) void attn_decode_split_bf16(Deco
   }
 
   if constexpr (COOP) {
-  // waves 1-3 hand their running maxima, row sums and O^T to wave 0 through
-  // LDS (O^T in their own, now idle, V buffers); wave 0 rescales each to the
-  // larger maximum and adds it (an empty quarter holds m = -inf, l = 0,
-  // O = 0 and adds nothing; wave 0 always has keys)
-  static_assert(DB * 16 * 64 * 4 <= 2 * kBlk * D * 2, "O^T fits a wave's two V buffers");
-  __shared__ float red_ml[kWavesDec][2][64];
-  if (wave > 0) {
-    SQA_LDS float* xo = (SQA_LDS float*)lds_v[wave][0];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) xo[(db * 16 + r) * 64 + lane] = o[db][r];
-    red_ml[wave][0][lane] = m_run;
-    red_ml[wave][1][lane] = l_run;
+    static_assert(DB * 16 * 64 * 4 <= 2 * kBlk * D * 2, "O^T fits a wave's two V buffers");
+    __shared__ float red_ml[kWavesDec][2][64];
+    // wave w's O^T goes to its own, now idle, V buffers
+    if (!coop_merge(o, m_run, l_run, wave, lane, [&](int w) { return (SQA_LDS float*)lds_v[w][0]; }, red_ml))
+      return;
   }
-  __syncthreads();
-  if (wave > 0) return;
+
+  const float l_tot = wave_pair_sum(l_run);
+  if (!valid) return;
+  const int64_t part = ((int64_t)b * p.H_q + h) * p.n_splits + split;
+  if (half == 0) *(float2*)(p.part_ml + part * 2) = make_float2(m_run, l_tot);
+  float* po = p.part_o + part * D;
+  // O^T[db] register r holds head dim db*32 + 8*(r/4) + 4*half + r%4
 #pragma unroll
-  for (int w = 1; w < kWavesDec; ++w) {
-    const SQA_LDS float* xo = (const SQA_LDS float*)lds_v[w][0];
-    const float mw = red_ml[w][0][lane];
-    const float m_new = fmaxf(m_run, mw);
-    const float a0 = __builtin_amdgcn_exp2f(m_run - m_new);
-    const float a1 = __builtin_amdgcn_exp2f(mw - m_new);
-    l_run = l_run * a0 + red_ml[w][1][lane] * a1;
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int j = 0; j < 4; ++j)
+      *(f32x4*)(po + db * 32 + 8 * j + 4 * half) =
+          (f32x4){o[db][4 * j], o[db][4 * j + 1], o[db][4 * j + 2], o[db][4 * j + 3]};
+}
+
+// fp32 split kernel: the bf16 kernel's split plan, unit mapping, softmax,
+// merge and partial-result layout, with both products on
+// v_mfma_f32_32x32x2_f32 (fp32 operands and sums).  S^T = K Q^T: lane
+// (key, half) supplies K[key][8j + 4*half + e] for k-step 4j + e from a
+// 16-byte load of its row, and the Q^T operand uses the same dim order.
+// O^T += V^T P^T: score register r supplies the key pair
+// 8*(r/4) + r%4 (+ 4 in the upper half), V^T comes straight from HBM (32
+// consecutive floats of a row per half-wave).  The next block's K and V are
+// loaded into registers while the current one is computed.
+template <int D, bool COOP>
+__global__ __launch_bounds__(kWavesDec * 64, 1) void attn_decode_split_f32(DecodeParams p) {
+  constexpr int DB = D / 32;   // 32-dim blocks of O^T
+  constexpr int NQ = D / 8;    // 16-byte groups per wave half of a row
+  constexpr int NV = 16 * DB;  // V operands per block
+  __shared__ float lds_x[COOP ? (kWavesDec - 1) * DB * 16 * 64 : 4];
+
+  const float* qg = (const float*)p.q;
+  const float* kg = (const float*)p.k;
+  const float* vg = (const float*)p.v;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  const int64_t uid = COOP ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * kWavesDec + wave;
+  if (!COOP && uid >= p.n_waves) return;   // wave-uniform; no barrier on this path
+  const int g = (int)(uid % p.H_kv);
+  const int64_t r1 = uid / p.H_kv;
+  const int hb = (int)(r1 % p.HB);
+  const int64_t r2 = r1 / p.HB;
+  const int split = (int)(r2 % p.n_splits);
+  const int b = (int)(r2 / p.n_splits);
+
+  const int len = cache_len(p, b);
+  const int ks0 = split * p.split_len;
+  if (ks0 >= len) return;         // empty split (uniform per unit): the combine step skips it
+  const int ks1 = min(ks0 + p.split_len, len);
+  const int q_blk = COOP ? ((ks1 - ks0 + kBlk - 1) / kBlk + kWavesDec - 1) / kWavesDec : 0;
+  const int k0 = COOP ? ks0 + wave * q_blk * kBlk : ks0;
+  const int k1 = COOP ? min(k0 + q_blk * kBlk, ks1) : ks1;
+  const int n_blk = k1 > k0 ? (k1 - k0 + kBlk - 1) / kBlk : 0;
+
+  const int hc = hb * 32 + col;   // query head of this lane's column, within the group
+  const bool valid = hc < p.R;
+  const int h = g * p.R + hc;
+
+  // Q^T operand: dims 8j + 4*half + e at qf[4j + e]; zero for columns past R
+  float qf[4 * NQ];
+  {
+    const float* qp = qg + ((int64_t)b * p.H_q + (valid ? h : g * p.R)) * D + 4 * half;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + xo[(db * 16 + r) * 64 + lane] * a1;
-      // keeps each wave's reads after the previous wave's sums
-      asm volatile("" : "+v"(o[db]));
+    for (int j = 0; j < NQ; ++j) {
+      const f32x4 x = *(const f32x4*)(qp + 8 * j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qf[4 * j + e] = valid ? __uint_as_float(__float_as_uint(x[e]) ^ p.q_sign) : 0.f;
     }
-    m_run = m_new;
   }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;
+
+  if (n_blk > 0) {
+    const int64_t kv_stride = (int64_t)p.H_kv * D;
+    const float* k_base = kg + ((int64_t)b * p.S_max * p.H_kv + g) * D;
+    const float* v_base = vg + ((int64_t)b * p.S_max * p.H_kv + g) * D;
+    const float c = p.c;
+    // block at row0: K of key row0 + col (dims 8j + 4*half ...), V of the keys
+    // of score register r at head dims db*32 + col; rows past k1 clamped
+    // (their scores are masked)
+    auto load = [&](f32x4 (&kd)[NQ], float (&vd)[NV], int row0) {
+      const float* kp = k_base + (int64_t)min(row0 + col, k1 - 1) * kv_stride + 4 * half;
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) kd[j] = *(const f32x4*)(kp + 8 * j);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float* vp = v_base + (int64_t)min(row0 + 8 * (r >> 2) + 4 * half + (r & 3), k1 - 1) * kv_stride + col;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) vd[r * DB + db] = vp[db * 32];
+      }
+    };
+    auto step = [&](int t, f32x4 (&kc)[NQ], float (&vc)[NV], f32x4 (&kn)[NQ], float (&vn)[NV]) {
+      const int r0 = k0 + t * kBlk;
+      if (t + 1 < n_blk) load(kn, vn, r0 + kBlk);
+      f32x16 s = (f32x16){};
+#pragma unroll
+      for (int j = 0; j < NQ; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_mfma_f32_32x32x2f32(kc[j][e], qf[4 * j + e], s, 0, 0, 0);
+      // keys past the split end: s[r] holds key r0 + 8*(r/4) + 4*half + r%4
+      if (r0 + kBlk > k1) {
+        const int lim = k1 - 1 - r0 - 4 * half;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + (r & 3) > lim) s[r] = -__builtin_inff();
+      }
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = wave_pair_max(mx);
+      const float m_cand = mx * c;
+      const bool grow = m_cand > m_run + kLazyLog2D;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? m_cand : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      }
+      const float neg_m = -m_run;
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, neg_m));
+        psum += s[r];
+      }
+      l_run += psum;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vc[r * DB + db], s[r], o[db], 0, 0, 0);
+    };
+    f32x4 ka[NQ], kb[NQ];
+    float va[NV], vb[NV];
+    load(ka, va, k0);
+    for (int t = 0; t < n_blk; t += 2) {
+      step(t, ka, va, kb, vb);
+      if (t + 1 < n_blk) step(t + 1, kb, vb, ka, va);
+    }
+  }
+
+  if constexpr (COOP) {
+    __shared__ float red_ml[kWavesDec][2][64];
+    if (!coop_merge(o, m_run, l_run, wave, lane,
+                    [&](int w) { return (SQA_LDS float*)lds_x + (w - 1) * DB * 16 * 64; }, red_ml))
+      return;
   }
 
   const float l_tot = wave_pair_sum(l_run);
@@ -304,8 +470,8 @@ __global__ __launch_bounds__(kWavesDec * 64, 2) void attn_decode_split_bf16(Deco
 // splits, each group with its own running maximum, then an LDS reduction
 // over the groups (a separate maximum pass before the weighted sum made this
 // kernel 0.2-0.3 us, about 5 %, slower).
-template <int D>
-__global__ __launch_bounds__(256) void attn_decode_combine_bf16(DecodeParams p) {
+template <int D, bool F32OUT>
+__global__ __launch_bounds__(256) void attn_decode_combine(DecodeParams p) {
   constexpr int DC = D / 32;            // dim chunks per head
   constexpr int LANES = 8;              // lanes per split group
   constexpr int SG = 256 / LANES;       // split groups
@@ -319,9 +485,13 @@ __global__ __launch_bounds__(256) void attn_decode_combine_bf16(DecodeParams p) 
   const int dc = blockIdx.x % DC;
   const int b = (int)(row / p.H_q);
   const int len = cache_len(p, b);
-  uint16_t* op = p.out + row * D + dc * 32;
+  uint16_t* op = p.out + row * D + dc * 32;             // bf16 output
+  float* opf = (float*)p.out + row * D + dc * 32;       // fp32 output
   if (len <= 0) {   // uniform over the workgroup
-    if (tid < 32) op[tid] = 0;
+    if (tid < 32) {
+      if constexpr (F32OUT) opf[tid] = 0.f;
+      else op[tid] = 0;
+    }
     if (p.lse && dc == 0 && tid == 0) p.lse[row] = -__builtin_inff();
     return;
   }
@@ -364,72 +534,16 @@ __global__ __launch_bounds__(256) void attn_decode_combine_bf16(DecodeParams p) 
       o += wg * red_o[g2][tid];
     }
     const float inv = 1.0f / Lt;
-    bf16x4 w4;
+    if constexpr (F32OUT) {
+      *(f32x4*)(opf + tid * 4) = o * inv;
+    } else {
+      bf16x4 w4;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w4[e] = (__bf16)(o[e] * inv);
-    *(bf16x4*)(op + tid * 4) = w4;
+      for (int e = 0; e < 4; ++e) w4[e] = (__bf16)(o[e] * inv);
+      *(bf16x4*)(op + tid * 4) = w4;
+    }
     if (p.lse && dc == 0 && tid == 0) p.lse[row] = (M + log2f(Lt)) * 0.69314718055994531f;
   }
-}
-
-// fp32 path: one thread per (b, h), online softmax over the cache in fp32.
-// Plain VALU arithmetic for exactness checks at small sizes.
-template <int D>
-__global__ __launch_bounds__(256) void attn_decode_f32(const float* __restrict__ q, const float* __restrict__ k,
-                                                       const float* __restrict__ v, const int32_t* __restrict__ seqlens,
-                                                       float* __restrict__ out, float* __restrict__ lse, int64_t B,
-                                                       int S_max, int H_q, int H_kv, int R, float c) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= B * H_q) return;
-  const int64_t b = t / H_q;
-  const int h = (int)(t % H_q);
-  const int g = h / R;
-  int len = seqlens ? seqlens[b] : S_max;
-  len = min(len, S_max);
-  float* op = out + t * D;
-  if (len <= 0) {
-#pragma unroll
-    for (int e = 0; e < D; ++e) op[e] = 0.f;
-    if (lse) lse[t] = -__builtin_inff();
-    return;
-  }
-  float qv[D], acc[D];
-#pragma unroll
-  for (int e = 0; e < D; ++e) {
-    qv[e] = q[t * D + e];
-    acc[e] = 0.f;
-  }
-  float m = -__builtin_inff(), l = 0.f;
-  for (int j = 0; j < len; ++j) {
-    const float* kp = k + ((b * S_max + j) * H_kv + g) * D;
-    const float* vp = v + ((b * S_max + j) * H_kv + g) * D;
-    float dot = 0.f;
-#pragma unroll
-    for (int e = 0; e < D; ++e) dot = __builtin_fmaf(qv[e], kp[e], dot);
-    const float x = dot * c;
-    const float m_new = fmaxf(m, x);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    const float pj = __builtin_amdgcn_exp2f(x - m_new);
-    m = m_new;
-    l = l * alpha + pj;
-#pragma unroll
-    for (int e = 0; e < D; ++e) acc[e] = __builtin_fmaf(pj, vp[e], acc[e] * alpha);
-  }
-  const float inv = 1.0f / l;
-#pragma unroll
-  for (int e = 0; e < D; ++e) op[e] = acc[e] * inv;
-  if (lse) lse[t] = (m + log2f(l)) * 0.69314718055994531f;
-}
-
-template <int D>
-hipError_t launch_decode_f32_t(const DecodeArgs& a) {
-  const int64_t threads = a.B * a.H_q;
-  // the fp32 kernel keeps the sign of the scale in c (no bf16 operand to negate)
-  const float c = a.negate_q ? -a.c : a.c;
-  hipLaunchKernelGGL((attn_decode_f32<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                     (hipStream_t)a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v, a.seqlens,
-                     (float*)a.out, a.lse, a.B, (int)a.S_max, a.H_q, a.H_kv, a.H_q / a.H_kv, c);
-  return hipGetLastError();
 }
 
 template <int D>
@@ -451,19 +565,29 @@ hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& plan) {
   p.n_splits = plan.n_splits;
   p.split_len = plan.split_len;
   p.c = a.c;
-  p.q_sign = a.negate_q ? 0x8000u : 0u;
+  p.q_sign = a.dtype == 1 ? (a.negate_q ? 0x80000000u : 0u) : (a.negate_q ? 0x8000u : 0u);
   p.n_waves = a.B * a.H_kv * plan.head_blocks * plan.n_splits;
-  if (plan.coop)
-    hipLaunchKernelGGL((attn_decode_split_bf16<D, true>), dim3((unsigned)plan.n_wgs), dim3(kWavesDec * 64), 0,
-                       (hipStream_t)a.stream, p);
-  else
-    hipLaunchKernelGGL((attn_decode_split_bf16<D, false>), dim3((unsigned)plan.n_wgs), dim3(kWavesDec * 64), 0,
-                       (hipStream_t)a.stream, p);
+  const dim3 grid((unsigned)plan.n_wgs), block(kWavesDec * 64);
+  if (a.dtype == 1) {
+    if (plan.coop)
+      hipLaunchKernelGGL((attn_decode_split_f32<D, true>), grid, block, 0, (hipStream_t)a.stream, p);
+    else
+      hipLaunchKernelGGL((attn_decode_split_f32<D, false>), grid, block, 0, (hipStream_t)a.stream, p);
+  } else {
+    if (plan.coop)
+      hipLaunchKernelGGL((attn_decode_split_bf16<D, true>), grid, block, 0, (hipStream_t)a.stream, p);
+    else
+      hipLaunchKernelGGL((attn_decode_split_bf16<D, false>), grid, block, 0, (hipStream_t)a.stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = a.B * a.H_q;
-  hipLaunchKernelGGL((attn_decode_combine_bf16<D>), dim3((unsigned)(rows * (D / 32))), dim3(256), 0,
-                     (hipStream_t)a.stream, p);
+  if (a.dtype == 1)
+    hipLaunchKernelGGL((attn_decode_combine<D, true>), dim3((unsigned)(rows * (D / 32))), dim3(256), 0,
+                       (hipStream_t)a.stream, p);
+  else
+    hipLaunchKernelGGL((attn_decode_combine<D, false>), dim3((unsigned)(rows * (D / 32))), dim3(256), 0,
+                       (hipStream_t)a.stream, p);
   return hipGetLastError();
 }
 
@@ -472,14 +596,6 @@ hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& plan) {
 namespace {
 
 hipError_t launch_decode_planned(const DecodeArgs& a, const DecodePlan& plan) {
-  if (a.dtype == 1) {
-    switch (a.d) {
-      case 32: return launch_decode_f32_t<32>(a);
-      case 64: return launch_decode_f32_t<64>(a);
-      case 128: return launch_decode_f32_t<128>(a);
-    }
-    return hipErrorInvalidValue;
-  }
   switch (a.d) {
     case 32: return launch_decode_t<32>(a, plan);
     case 64: return launch_decode_t<64>(a, plan);
@@ -533,7 +649,6 @@ hipError_t launch_attn_decode(const DecodeArgs& a) {
 
 hipError_t launch_attn_decode_noalloc(const DecodeArgs& a) {
   const DecodePlan plan = decode_plan(a.B, a.S_max, a.H_q, a.H_kv, a.d, kDecodeScratchBytes);
-  if (a.dtype == 1) return launch_decode_planned(a, plan);   // the fp32 kernel uses no workspace
   if (plan.workspace_bytes > kDecodeScratchBytes) return hipErrorInvalidValue;
   DecodeArgs b = a;
   int device = -1;

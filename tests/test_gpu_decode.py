@@ -178,3 +178,25 @@ def test_decode_f32(d):
     assert (got[2] == 0).all() and np.isneginf(lse[2].cpu().numpy()).all()
     parity.check(got[:2], ref[:2], "f32", f"decode f32 d={d}")
     assert np.abs(lse[:2].double().cpu().numpy() - ref_lse[:2]).max() < 2e-5
+# fp32 on the matrix cores at longer caches: independent waves (eight K/V
+# heads), the shared four-wave splits (one K/V head), ragged lengths.
+F32_LONG = [(2, 3000, 32, 8, 128, [3000, 1777]), (1, 5000, 32, 1, 64, [4999]), (3, 2100, 6, 2, 32, [2100, 64, 65])]
+
+
+@pytest.mark.parametrize("B,S_max,H_q,H_kv,d,lens", F32_LONG)
+def test_decode_f32_long(B, S_max, H_q, H_kv, d, lens):
+    _say(f"decode f32 B={B} S_max={S_max} H={H_q}/{H_kv} d={d} lens={lens}")
+    seed = 8300 + S_max + d
+    q = inputs.normal(seed, 0, (B, H_q, d), "f32")
+    k = inputs.normal(seed, 1, (B, S_max, H_kv, d), "f32")
+    v = inputs.normal(seed, 2, (B, S_max, H_kv, d), "f32")
+    dq, dk, dv = gpu_util.to_device(q), gpu_util.to_device(k), gpu_util.to_device(v)
+    dl = torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
+    for scale in (1 / math.sqrt(d), -0.3):
+        out, lse = sqa.attn_decode(dq, dk, dv, seqlens=dl, scale=scale, return_lse=True)
+        torch.cuda.synchronize()
+        ref, ref_lse = oracle.decode(q, k, v, float(np.float32(scale)), seqlens=lens)
+        parity.check(out.double().cpu().numpy(), ref, "f32", f"decode f32 scale={scale}")
+        assert np.abs(lse.double().cpu().numpy() - ref_lse).max() < 2e-5
+
+
