@@ -462,9 +462,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_f32(F32Params p) {
   constexpr int KP = D / 2;   // MFMA k-steps over the head dimension (two dims each)
   constexpr int DB = D / 32;  // 32-row blocks of O^T
   constexpr int KB = 32;      // keys per tile
-  constexpr int LD = D + 1;   // LDS row stride in floats
-  constexpr int F4 = KB * D / 4 / (WAVES * 64);  // 16-byte copies per thread and matrix
-  static_assert(F4 >= 1 && (KB * D / 4) % (WAVES * 64) == 0, "tile copies must split evenly");
+  constexpr int LD = F32Tile<D>::LD;   // LDS row stride in floats
   __shared__ float lds_k[2][KB * LD];
   __shared__ float lds_v[2][KB * LD];
 
@@ -489,34 +487,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_f32(F32Params p) {
   const int wg_last_pos = min((last_item / p.R) * 32 + 31, S - 1);
   const int n_tiles = CAUSAL ? wg_last_pos / KB + 1 : (S + KB - 1) / KB;
 
-  // tile copies: thread tid moves 16-byte chunks j * 256 + tid of the tile
-  // (row = chunk / (D/4)); key rows past S are clamped (masked in the scores)
+  // K and V tiles through registers (rows past S clamped, masked in the scores)
   const float* k_base = p.k + (int64_t)b * S * p.kv_stride + g * D;
   const float* v_base = p.v + (int64_t)b * S * p.kv_stride + g * D;
-  f32x4 rk[F4], rv[F4];
-  auto load = [&](int t) {
-#pragma unroll
-    for (int j = 0; j < F4; ++j) {
-      const int idx = j * WAVES * 64 + tid;
-      const int row = idx / (D / 4);
-      const int64_t off = (int64_t)min(t * KB + row, S - 1) * p.kv_stride + 4 * (idx % (D / 4));
-      rk[j] = *(const f32x4*)(k_base + off);
-      rv[j] = *(const f32x4*)(v_base + off);
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < F4; ++j) {
-      const int idx = j * WAVES * 64 + tid;
-      const int o = (idx / (D / 4)) * LD + 4 * (idx % (D / 4));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lds_k[buf][o + e] = rk[j][e];
-        lds_v[buf][o + e] = rv[j][e];
-      }
-    }
-  };
-  load(0);
+  F32Tile<D> tk, tv;
+  tk.load(k_base, p.kv_stride, 0, S, tid);
+  tv.load(v_base, p.kv_stride, 0, S, tid);
 
   // Q^T as the B operand: lane holds query pos0 + col, dims 2*ks + half
   float qf[KP];
@@ -536,13 +512,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_f32(F32Params p) {
   const int my_q = pos0 + col;
   const int wave_last = pos0 + 31;
 
-  store(0);
-  if (n_tiles > 1) load(1);
+  tk.store(lds_k[0], tid);
+  tv.store(lds_v[0], tid);
+  if (n_tiles > 1) {
+    tk.load(k_base, p.kv_stride, KB, S, tid);
+    tv.load(v_base, p.kv_stride, KB, S, tid);
+  }
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
     __syncthreads();   // tile t stored by everyone; tile t-1 fully consumed
-    if (t + 1 < n_tiles) store(buf ^ 1);
-    if (t + 2 < n_tiles) load(t + 2);
+    if (t + 1 < n_tiles) {
+      tk.store(lds_k[buf ^ 1], tid);
+      tv.store(lds_v[buf ^ 1], tid);
+    }
+    if (t + 2 < n_tiles) {
+      tk.load(k_base, p.kv_stride, (t + 2) * KB, S, tid);
+      tv.load(v_base, p.kv_stride, (t + 2) * KB, S, tid);
+    }
     const int kv0 = t * KB;
     if (!active || (CAUSAL && kv0 > wave_last)) continue;
     const float* kt = lds_k[buf];

@@ -127,6 +127,36 @@ struct TileCopy {
   }
 };
 
+// fp32 kernels: tiles of 32 rows of D floats (256 threads) staged through
+// registers into LDS rows padded
+// by one float (an MFMA operand that reads a column -- 32 rows at one
+// dim -- hits 32 distinct banks).  Thread tid moves 16-byte chunks
+// j * 256 + tid; rows at or past S are clamped to S - 1 (in bounds; their
+// contributions are masked).
+template <int D>
+struct F32Tile {
+  static constexpr int LD = D + 1;
+  static constexpr int F4 = 32 * D / 4 / 256;
+  static_assert(F4 >= 1 && (32 * D / 4) % 256 == 0, "tile copies must split evenly");
+  f32x4 r[F4];
+  __device__ __forceinline__ void load(const float* base, int64_t stride, int row0, int S, int tid) {
+#pragma unroll
+    for (int j = 0; j < F4; ++j) {
+      const int idx = j * 256 + tid;
+      r[j] = *(const f32x4*)(base + (int64_t)min(row0 + idx / (D / 4), S - 1) * stride + 4 * (idx % (D / 4)));
+    }
+  }
+  __device__ __forceinline__ void store(float* lds, int tid) const {
+#pragma unroll
+    for (int j = 0; j < F4; ++j) {
+      const int idx = j * 256 + tid;
+      const int o = (idx / (D / 4)) * LD + 4 * (idx % (D / 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lds[o + e] = r[j][e];
+    }
+  }
+};
+
 }  // namespace dev
 }  // namespace sqa
 
