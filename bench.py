@@ -141,6 +141,57 @@ def time_backward(sqa, torch, w, variant, steps, warmup):
             "kernels": "bwd_stats_bf16 + bwd_dq_bf16 + bwd_dkdv_bf16 (one sqa_attn_bwd call)"}
 
 
+def time_fp32(sqa, torch, steps, warmup):
+    """fp32 inputs on the fp32 matrix cores: forward and backward at the
+    S = 4096, d = 64 MHA 16/16 shape (the sweep's inputs widened exactly to
+    fp32, a seeded N(0,1) upstream gradient), against the 157.3 TFLOP/s fp32
+    matrix peak; the backward is credited at 10*d flops per pair, as for
+    bf16."""
+    import inputs
+    import inputs.configs as cfg
+    sw = cfg.WORKLOADS["sweep_s4096"]
+    name = "mha"
+    v = sw.variant(name)
+    q, k, vv, _ = cfg.make_inputs(sw, name)
+    g = inputs.normal(sw.seed(name), 5, q.shape, "f32", 1.0)
+    tq, tk, tv = (torch.from_numpy(inputs.bf16_bits_to_f32(a)).to("cuda") for a in (q, k, vv))
+    tg = torch.from_numpy(g).to("cuda")
+    del q, k, vv, g
+    stream = torch.cuda.current_stream()
+    out = torch.empty_like(tq)
+    lse = torch.empty((sw.B, sw.S, v.H_q), dtype=torch.float32, device="cuda")
+    gq, gk, gv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+    ws = torch.empty(sqa.attn_bwd_workspace_size(sw.B, sw.S, v.H_q), dtype=torch.uint8, device="cuda")
+
+    def fwd():
+        sqa.attn_fwd(tq, tk, tv, out=out, lse=lse, scale=sw.scale, causal=sw.causal, stream=stream)
+
+    def bwd():
+        sqa.attn_bwd(tq, tk, tv, out, tg, lse, scale=sw.scale, causal=sw.causal, stream=stream,
+                     dq=gq, dk=gk, dv=gv, workspace=ws)
+
+    flops = algorithmic_flops(sw.B, sw.S, v.H_q, sw.d, sw.causal)
+    res = {"workload": f"{sw.name}/{name}", "dtype": "f32", "B": sw.B, "S": sw.S, "H_q": v.H_q, "H_kv": v.H_kv,
+           "d": sw.d, "peak_tflops": PEAK_FP32_TFLOPS}
+    for label, fn, fl in (("forward", fwd, flops), ("backward", bwd, flops * 10 // 4)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tf = fl / (ms * 1e-3) / 1e12
+        res[label] = {"ms_per_step": round(ms, 4), "flops": fl, "tflops": round(tf, 2),
+                      "pct_fp32_peak": round(100 * tf / PEAK_FP32_TFLOPS, 2)}
+    del tq, tk, tv, tg, out, lse, gq, gk, gv, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_decode(sqa, torch, wname, steps, warmup):
     """Decode (one token per sequence against its K/V cache) for every head
     configuration of the decode workload, on the same cache lengths.
@@ -517,6 +568,8 @@ def main():
     ap.add_argument("--layer", choices=["auto", "none", "only"], default="auto",
                     help="time the full attention layer too (auto), or only it")
     ap.add_argument("--layer-workload", default="layer_s32k")
+    ap.add_argument("--fp32", choices=["auto", "none"], default="auto",
+                    help="time the fp32 forward and backward at the S=4096 MHA shape too")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB (HBM counter calibration)")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -621,6 +674,7 @@ def main():
            if args.backward == "auto" and w.dtype == "bf16" else None)
     dec = time_decode(sqa, torch, args.decode_workload, 20, 3) if args.decode == "auto" else None
     lay = time_layer(sqa, torch, args.layer_workload, 5, 2) if args.layer == "auto" else None
+    f32 = time_fp32(sqa, torch, 20, 3) if args.fp32 == "auto" else None
     cpu = cpu_baseline(w, args.variant, args.cpu_budget) if args.cpu_budget > 0 else None
     if cpu is not None and args.cpu_full == "auto":
         # the two workloads the oracle finishes whole in seconds
@@ -658,6 +712,7 @@ def main():
         "backward": bwd,
         "decode": dec,
         "layer": lay,
+        "fp32": f32,
         "cpu_baseline": cpu,
         "pages_claim": "SQA abstract: up to 3x throughput on 32k-200k sequences; hardware not named",
         "context_library_gemm": gemm,
