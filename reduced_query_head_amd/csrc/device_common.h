@@ -128,10 +128,11 @@ struct TileCopy {
 };
 
 // fp32 kernels: tiles of 32 rows of D floats (256 threads) staged through
-// registers into LDS rows padded by one float (an MFMA operand that reads a
-// column -- 32 rows at one dim -- hits 32 distinct banks).  Thread tid moves
-// 16-byte chunks j * 256 + tid; rows at or past S are clamped to S - 1 (in
-// bounds; their contributions are masked).
+// registers into LDS rows padded
+// by one float (an MFMA operand that reads a column -- 32 rows at one
+// dim -- hits 32 distinct banks).  Thread tid moves 16-byte chunks
+// j * 256 + tid; rows at or past S are clamped to S - 1 (in bounds; their
+// contributions are masked).
 template <int D>
 struct F32Tile {
   static constexpr int LD = D + 1;
