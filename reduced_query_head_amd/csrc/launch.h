@@ -14,6 +14,7 @@ constexpr int kBwdWaves = 4;      // waves of a dq workgroup (a dk/dv workgroup 
 constexpr int kDkdvChunk = 32;    // key blocks of one group an XCD takes in a row (long sequences)
 constexpr int kDecodeBlk = 32;    // keys per decode block (one S^T MFMA tile)
 constexpr int kDecodeWaves = 4;   // waves per decode split (one workgroup)
+constexpr int kDecodeCUs = 256;   // compute units a shared-split decode plan fills (MI355X)
 constexpr int64_t kLayerGemmWorkspace = (int64_t)32 << 20;   // bytes offered to the GEMM library
 
 // rows padded to the backward's 64-row tiles

@@ -52,11 +52,17 @@ int64_t bwd_grid_size(int64_t B, int64_t S, int32_t H_q, int32_t H_kv) {
 // faster).  Each wave has at least 64 keys, and at least 16 keys per query
 // head it serves, so the fp32 partial results written per split stay a
 // small share of the cache bytes it reads.  With fewer K/V heads than waves
-// per workgroup (coop), a split is the range of kDecodeWaves such waves (one
-// workgroup, merged in LDS): a quarter of the partial results.  With more,
-// each wave is a split of its own and a workgroup's waves read neighbouring
-// heads of the same positions (measured 7-11 % faster there than the
-// cooperative splits, which read one head).
+// per workgroup (coop), a split is the range of kDecodeWaves waves (one
+// workgroup, merged in LDS), so one partial result covers four waves' keys;
+// there the plan is one workgroup per CU instead, each wave at least 64
+// keys, with no floor per served head.  Against the per-wave rule (A/B, one
+// box, mixed cache lengths): 4 x 128K MQA 8/1 42.5 -> 39.4 us, GQA 32/2
+// 97.3 -> 87.1 us, 8 x 128K GQA 32/2 169.9 -> 141.2 us, 1 x 32K MQA 32/1
+// 27.0 -> 13.1 us (128 workgroups instead of 16), MQA 32/1 at 4 x 128K
+// unchanged; 16 x 16K GQA 32/2 lost 5 %.  With four or more K/V heads each
+// wave is a split of its own and a workgroup's waves read neighbouring heads
+// of the same positions (measured 7-11 % faster there than the cooperative
+// splits, which read one head).
 DecodePlan decode_plan(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d, int64_t max_workspace) {
   DecodePlan pl;
   const int64_t R = H_q / H_kv;
@@ -69,10 +75,16 @@ DecodePlan decode_plan(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int3
     const int64_t len_floor = S_max * units / floor_waves;  // keeps >= floor_waves waves
     len = len_floor < 512 ? (len_floor > len ? len_floor : len) : 512;
   }
-  if (len < 64) len = 64;
-  if (len < 16 * heads_per_wave) len = 16 * heads_per_wave;
-  len = (len + kDecodeBlk - 1) / kDecodeBlk * kDecodeBlk;
   pl.coop = H_kv < kDecodeWaves;
+  if (pl.coop && units > 0) {
+    // shared splits: one workgroup per CU, each wave a quarter of its split
+    len = (S_max * units + kDecodeCUs * kDecodeWaves - 1) / (kDecodeCUs * kDecodeWaves);
+    if (len < 64) len = 64;
+  } else {
+    if (len < 64) len = 64;
+    if (len < 16 * heads_per_wave) len = 16 * heads_per_wave;
+  }
+  len = (len + kDecodeBlk - 1) / kDecodeBlk * kDecodeBlk;
   if (pl.coop) len *= kDecodeWaves;   // keys per split
   // a workspace bound: at most max_workspace / (bytes per split of every
   // head) splits, so each split covers at least S_max / that many keys

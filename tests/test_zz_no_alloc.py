@@ -86,11 +86,11 @@ def test_noalloc_equals_workspace_decode_two_calls():
 
 
 def test_noalloc_longer_splits_then_smaller_call():
-    """Eight 64/1 caches of 128K positions: the workspace call's plan needs
+    """Eight 32/4 caches of 128K positions: the workspace call's plan needs
     more than the 16 MiB scratch, so the allocation-free call takes longer
     splits (same sum, other rounding).  Then a smaller call reuses the
     scratch."""
-    B, S_max, H_q, H_kv, d = 8, 131072, 64, 1, 128
+    B, S_max, H_q, H_kv, d = 8, 131072, 32, 4, 128
     need = sqa.attn_decode_workspace_size(B, S_max, H_q, H_kv, d)
     assert need > (16 << 20), need
     lens = [131072, 70000, 1, 0, 513, 4096, 99999, 32]
