@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_BYTES_PER_S = 8.0e12
+DECODE_GRAPH_REPLAYS = 5
 KERNEL_SOURCES = ["reduced_query_head_amd/csrc/attn_fwd.hip", "reduced_query_head_amd/csrc/device_common.h"]
 
 
@@ -212,30 +213,53 @@ def time_decode(sqa, torch, wname, steps, warmup):
                          device="cuda")
         stream = torch.cuda.current_stream()
 
-        def run():
-            sqa.attn_decode(dq_, dk_, dv_, seqlens=dl, out=out, lse=lse, scale=w.scale, stream=stream, workspace=ws)
+        def run(st):
+            sqa.attn_decode(dq_, dk_, dv_, seqlens=dl, out=out, lse=lse, scale=w.scale, stream=st, workspace=ws)
         for _ in range(warmup):
-            run()
+            run(stream)
         torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         ev[0].record(stream)
         for i in range(steps):
-            run()
+            run(stream)
             ev[i + 1].record(stream)
         torch.cuda.synchronize()
         per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
         ms = sum(per) / steps
+        # the same calls replayed from a HIP graph, as a serving loop runs its
+        # decode steps: device time per call without the binding's host work
+        # between calls (the eager figure above includes it)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream()
+            for _ in range(steps):
+                run(cap)
+        graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(DECODE_GRAPH_REPLAYS):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        g_ms = g0.elapsed_time(g1) / (DECODE_GRAPH_REPLAYS * steps)
+        del graph
         nbytes = int(lens.sum()) * var.H_kv * w.d * 2 * 2 + 2 * w.B * var.H_q * w.d * 2 + w.B * var.H_q * 4
         res[var.name] = {"H_q": var.H_q, "H_kv": var.H_kv, "ms_per_call": round(ms, 4), "min_ms": round(min(per), 4),
                          "bytes_per_call": nbytes, "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
                          "frac_hbm_peak": round(nbytes / (ms * 1e-3) / PEAK_HBM_BYTES_PER_S, 4),
-                         "tokens_per_s": round(w.B / (ms * 1e-3), 1)}
+                         "tokens_per_s": round(w.B / (ms * 1e-3), 1),
+                         "graph_ms_per_call": round(g_ms, 4),
+                         "graph_GB_per_s": round(nbytes / (g_ms * 1e-3) / 1e9, 1),
+                         "graph_frac_hbm_peak": round(nbytes / (g_ms * 1e-3) / PEAK_HBM_BYTES_PER_S, 4)}
         del dq_, dk_, dv_, dl, out, lse, ws
         torch.cuda.empty_cache()
     return {"workload": w.name, "B": w.B, "S_max": w.S_max, "d": w.d,
             "cache_lengths": [int(x) for x in decode_lengths(w.seed(w.variants[0].name), w.B, w.S_max,
                                                              w.min_len_frac)], "variants": res,
-            "kernels": "attn_decode_split_bf16 + attn_decode_combine (one sqa_attn_decode call)"}
+            "kernels": "attn_decode_split_bf16 + attn_decode_combine (one sqa_attn_decode call)",
+            "timing": (f"ms_per_call: eager calls through the binding, events around each; graph_ms_per_call: "
+                       f"{steps} calls captured in one HIP graph, replayed {DECODE_GRAPH_REPLAYS} times")}
 
 
 def time_layer(sqa, torch, wname, steps, warmup):
