@@ -144,8 +144,10 @@ sqa_status sqa_attn_fwd_lse(const void* q, const void* k, const void* v, void* o
  *                        forward that produced out and lse)
  *
  * Outputs and workspace must not overlap each other or any input.  Errors as
- * for sqa_attn_fwd.  bf16: MFMA kernels with fp32 accumulation, probabilities and dS
- * rounded to bf16 for the products; fp32: plain fp32 arithmetic.
+ * for sqa_attn_fwd, and SQA_ERR_UNSUPPORTED when the workspace size would not
+ * fit int64.  bf16: MFMA kernels with fp32 accumulation, probabilities and dS
+ * rounded to bf16 for the products; fp32: fp32 MFMA kernels with fp32
+ * probabilities and dS.
  */
 sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                         const float* lse, void* dq, void* dk, void* dv, void* workspace,
@@ -153,7 +155,8 @@ sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, const void*
                         int32_t d, sqa_dtype dtype, float scale, int causal, sqa_stream_t stream);
 
 /* Workspace bytes sqa_attn_bwd needs (2 fp32 values per query row and head,
- * rows padded to a multiple of 64); -1 for invalid sizes. */
+ * rows padded to a multiple of 64); -1 for invalid sizes or a size beyond
+ * int64. */
 int64_t sqa_attn_bwd_workspace_size(int64_t B, int64_t S, int32_t H_q);
 
 /*
@@ -185,7 +188,8 @@ int64_t sqa_attn_bwd_workspace_size(int64_t B, int64_t S, int32_t H_q);
  * Outputs and workspace must not overlap each other or any input.
  * SQA_ERR_INVALID_ARGUMENT as for sqa_attn_fwd (and for a short workspace);
  * SQA_ERR_UNSUPPORTED for d not in {32, 64, 128}, H_q * d or H_kv * d above
- * 2^22, or S_max > 2^30.  B == 0
+ * 2^22, S_max > 2^30, or B * S_max * H_q * (d + 2) * 4 beyond int64 (the
+ * split plan's bound).  B == 0
  * is a successful no-op.  Asynchronous on `stream`.  A split kernel and a
  * combine kernel: bf16 MFMA with fp32 accumulation and probabilities rounded
  * to bf16 for the P.V product, or fp32 MFMA with fp32 probabilities.
@@ -195,7 +199,8 @@ sqa_status sqa_attn_decode(const void* q, const void* k_cache, const void* v_cac
                            int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d, sqa_dtype dtype, float scale,
                            sqa_stream_t stream);
 
-/* Workspace bytes sqa_attn_decode needs; -1 for invalid sizes. */
+/* Workspace bytes sqa_attn_decode needs; -1 for invalid sizes or a split
+ * plan beyond int64 (B * max(S_max, 1) * H_q * (d + 2) * 4). */
 int64_t sqa_attn_decode_workspace_size(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d);
 
 /*

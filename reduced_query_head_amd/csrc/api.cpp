@@ -2,6 +2,7 @@
 // Every check runs before any HIP call, so a rejected call has no effect.
 #include <math.h>
 #include <stdint.h>
+#include <initializer_list>
 
 #include "../../include/sqa.h"
 #include "launch.h"
@@ -22,6 +23,25 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   if (a != 0 && b > INT64_MAX / a) return false;
   *out = a * b;
   return true;
+}
+
+// true when the product of the non-negative factors stays within int64
+bool prod_ok(std::initializer_list<int64_t> factors) {
+  int64_t x = 1;
+  for (const int64_t f : factors)
+    if (!mul_ok(x, f, &x)) return false;
+  return true;
+}
+
+// Every product the decode split plan forms (keys x units, partial-result
+// bytes, workgroups) is at most B * max(S_max, 1) * H_q * (d + 2) * 4.
+bool decode_plan_fits(int64_t B, int64_t S_max, int32_t H_q, int32_t d) {
+  return prod_ok({B, S_max > 0 ? S_max : 1, H_q, (int64_t)d + 2, 4});
+}
+
+// The backward's workspace and statistics grid are at most 8 * B * H_q * (S + 64).
+bool bwd_plan_fits(int64_t B, int64_t S, int32_t H_q) {
+  return S <= INT64_MAX - 64 && prod_ok({B, S + 64, H_q, 8});
 }
 
 // Kernels address a tile of up to 128 rows relative to a 64-bit tile base
@@ -115,7 +135,7 @@ SQA_API sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, voi
 }
 
 SQA_API int64_t sqa_attn_bwd_workspace_size(int64_t B, int64_t S, int32_t H_q) {
-  if (B < 0 || S < 0 || H_q < 1) return -1;
+  if (B < 0 || S < 0 || H_q < 1 || !bwd_plan_fits(B, S, H_q)) return -1;
   return sqa::bwd_workspace_bytes(B, S, H_q);
 }
 
@@ -139,6 +159,7 @@ SQA_API sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, con
       !mul_ok(rows, (int64_t)H_kv * d, &kv_elems) || !mul_ok(q_elems, elem, &q_bytes) ||
       !mul_ok(kv_elems, elem, &kv_bytes) || !mul_ok(rows, (int64_t)H_q * 4, &lse_bytes))
     return SQA_ERR_INVALID_ARGUMENT;
+  if (!bwd_plan_fits(B, S, H_q)) return SQA_ERR_UNSUPPORTED;
   const int64_t ws_need = sqa::bwd_workspace_bytes(B, S, H_q);
   if (workspace_bytes < ws_need) return SQA_ERR_INVALID_ARGUMENT;
   // outputs and workspace must not overlap each other or any input
@@ -192,7 +213,7 @@ SQA_API sqa_status sqa_attn_bwd(const void* q, const void* k, const void* v, con
 
 SQA_API int64_t sqa_attn_decode_workspace_size(int64_t B, int64_t S_max, int32_t H_q, int32_t H_kv, int32_t d) {
   if (B < 0 || S_max < 0 || H_q < 1 || H_kv < 1 || H_q % H_kv != 0 || d < 1) return -1;
-  if (S_max > (int64_t)1 << 30 || B > ((int64_t)1 << 31)) return -1;
+  if (S_max > (int64_t)1 << 30 || B > ((int64_t)1 << 31) || !decode_plan_fits(B, S_max, H_q, d)) return -1;
   return sqa::decode_plan(B, S_max, H_q, H_kv, d).workspace_bytes;
 }
 
@@ -222,6 +243,7 @@ sqa_status decode_checks(const void* q, const void* k_cache, const void* v_cache
       !mul_ok(B, S_max, &cache_rows) || !mul_ok(cache_rows, (int64_t)H_kv * d, &kv_elems) ||
       !mul_ok(kv_elems, elem, &kv_bytes) || !mul_ok(B, (int64_t)H_q * 4, &lse_bytes))
     return SQA_ERR_INVALID_ARGUMENT;
+  if (!decode_plan_fits(B, S_max, H_q, d)) return SQA_ERR_UNSUPPORTED;
   const sqa::DecodePlan plan =
       sqa::decode_plan(B, S_max, H_q, H_kv, d, no_alloc ? sqa::kDecodeScratchBytes : 0);
   if (!no_alloc && workspace_bytes < plan.workspace_bytes) return SQA_ERR_INVALID_ARGUMENT;

@@ -125,6 +125,9 @@ def test_bwd_workspace_size():
     assert sqa.attn_bwd_workspace_size(2, 100, 8) == 2 * 2 * 8 * 128 * 4
     assert sqa.attn_bwd_workspace_size(1, 128, 1) == 2 * 128 * 4
     assert sqa.attn_bwd_workspace_size(-1, 10, 1) == -1
+    # sizes whose workspace is not representable in int64
+    assert sqa.attn_bwd_workspace_size(1 << 31, 1 << 30, 1 << 20) == -1
+    assert sqa.attn_bwd_workspace_size(1, (1 << 63) - 1, 1) == -1
 
 
 @pytest.mark.parametrize("kw", [
@@ -161,7 +164,8 @@ def test_decode_workspace_size():
     assert n >= 4 * 32 * (128 + 2) * 4
     assert sqa.attn_decode_workspace_size(4, 0, 32, 8, 128) > 0
     for bad in [(-1, 10, 4, 2, 64), (1, -1, 4, 2, 64), (1, 10, 0, 1, 64), (1, 10, 6, 4, 64), (1, 10, 4, 2, 0),
-                (1, (1 << 30) + 1, 4, 2, 64)]:
+                (1, (1 << 30) + 1, 4, 2, 64),
+                (1 << 20, 1 << 30, 1 << 20, 1, 32)]:      # a split plan beyond int64
         assert sqa.attn_decode_workspace_size(*bad) == -1
 
 
@@ -181,7 +185,11 @@ def test_decode_invalid(kw):
     assert _call_dec(**kw) == sqa.SQA_ERR_INVALID_ARGUMENT
 
 
-@pytest.mark.parametrize("kw", [dict(d=96), dict(d=16), dict(d=256), dict(dtype=1, d=96)])
+@pytest.mark.parametrize("kw", [dict(d=96), dict(d=16), dict(d=256), dict(dtype=1, d=96),
+                                # caches and q fit int64, the split plan over all 2^20 query heads does not
+                                dict(B=1 << 20, S_max=1 << 30, H_q=1 << 20, H_kv=1, d=32, ws_bytes=1 << 40,
+                                     q=FAKE, k=FAKE + (1 << 58), v=FAKE + (1 << 59), seqlens=0, out=FAKE + (3 << 58),
+                                     lse=0, ws=FAKE + (7 << 57))])
 def test_decode_unsupported(kw):
     assert _call_dec(**kw) == sqa.SQA_ERR_UNSUPPORTED
 
