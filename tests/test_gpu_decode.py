@@ -83,6 +83,10 @@ CASES = [
     # many short sequences: seeded lengths in [0, 600] with 0, 1 and over-long entries
     (64, 512, 32, 8, 128, [0, 1, 600] + [int(x) for x in np.random.default_rng(64).integers(0, 601, 61)]),
     (2, 1000, 128, 1, 64, [1000, 517]),      # 128 heads per group: four head blocks
+    # shared splits (fewer than 4 K/V heads) over long caches: many splits,
+    # lengths ending inside a split and inside a wave's quarter of one
+    (3, 40000, 32, 1, 128, [40000, 12345, 257]),
+    (2, 70001, 8, 2, 64, [70001, 33333]),
 ]
 
 
