@@ -31,9 +31,10 @@
 //    s - lse2/c and dP - D: P = 2^(c acc) and dS = P acc' with no per-score
 //    subtraction.
 //
-// All matrix products are bf16 MFMA with fp32 accumulation; P and dS are
-// rounded to bf16 for the products that consume them.  The fp32 path is plain
-// VALU arithmetic for exactness checks at small sizes.
+// bf16 inputs: all matrix products are bf16 MFMA with fp32 accumulation; P
+// and dS are rounded to bf16 for the products that consume them.  fp32
+// inputs: the same two-kernel split (bwd_dq_f32, bwd_dkdv_f32) on
+// v_mfma_f32_32x32x2_f32, with P and dS kept in fp32.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
