@@ -196,6 +196,12 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
   // faster on the 32K-200K workloads and 3-4 % at d = 64 (S = 4096 and 32K,
   // non-causal), where the softmax's VALU work is the tighter bound.
   constexpr bool ROWMFMA = D == 128 || (D == 64 && !CAUSAL && WAVES >= 8);
+  // d = 64 and 128 without the log-normaliser: the softmax shift is the
+  // maximum of the wave's first tile and stays fixed (no maximum on later
+  // tiles; 3-4 % faster at d = 128, up to 5 % at d = 64).  d = 32 keeps a
+  // running maximum on every tile: there the fixed shift's range check took
+  // a register past the 4-waves-per-SIMD budget.
+  constexpr bool FIXED_SHIFT = D >= 64;
   f32x4 lsum = (f32x4){0.f, 0.f, 0.f, 0.f};
   bf16x8 rs_sel;
   {
@@ -206,11 +212,17 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
   // lane l accumulates the row sum of the query of lane l ^ 16 for
   // 16 <= l < 48, of its own query otherwise
   const int rs_src = (lane >= 16 && lane < 48) ? (lane ^ 16) : lane;
+  // with the log-normaliser requested, the running maximum: its dominant
+  // probabilities are then close to 1 and exact in bf16, which the log of
+  // the row sum needs (with a fixed shift a dominant p keeps an arbitrary
+  // mantissa, whose bf16 rounding, up to 2^-8, goes into ln l unchanged)
+  const bool track_max = p.lse != nullptr;
   const float c = p.c;
   const int my_q = pos0 + col;
   const int wave_last = pos0 + kRows - 1;
 
-  auto step = [&](int t, SQA_LDS uint16_t* kt_cur, SQA_LDS uint16_t* vt_cur, SQA_LDS uint16_t* kt_nxt, SQA_LDS uint16_t* vt_nxt) {
+  auto step = [&](int t, SQA_LDS uint16_t* kt_cur, SQA_LDS uint16_t* vt_cur, SQA_LDS uint16_t* kt_nxt, SQA_LDS uint16_t* vt_nxt,
+                  bool first) {
     const int kv0l = t * KEYS;                // first key of the tile within the part
     const int kv0 = t_first * KEYS + kv0l;    // and within the sequence
     wait_copies();     // this wave's copies of tile t landed
@@ -257,29 +269,46 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
           if (nb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[nb][r] = -__builtin_inff();
     }
 
-    // online softmax in the exp2 domain: p = 2^(c*s - m).  The running max m
-    // is only moved when a row's maximum grows by more than 2^kLazyLog2, so
-    // p <= 2^kLazyLog2 and the accumulator is rarely rescaled; the result is
-    // the same for any m (it cancels in the final division by the row sum).
-    float mx = -__builtin_inff();
+    // online softmax in the exp2 domain: p = 2^(c*s - m); the result is the
+    // same for any shift m (it cancels in the final division by the row
+    // sum), which only has to keep p and O in range.  Fixed shift: m is the
+    // maximum of the wave's first tile (every row sees a key there) and stays
+    // fixed; a later score far above it could overflow p or O, which the
+    // range check after the key loop catches, and the rows are then
+    // recomputed with a running maximum.
+    if (FIXED_SHIFT && !track_max) {
+      if (first) {
+        float mx = -__builtin_inff();
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][r]);
-    mx = wave_pair_max(mx);
-    const float m_cand = mx * c;
-    const bool grow = m_cand > m_run + kLazyLog2;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float m_new = grow ? m_cand : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-      if constexpr (ROWMFMA) {
-        const float a_rs = __int_as_float(__builtin_amdgcn_ds_bpermute(rs_src * 4, __float_as_int(alpha)));
-        lsum *= a_rs;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][r]);
+        mx = wave_pair_max(mx);
+        m_run = mx > -__builtin_inff() ? mx * c : 0.f;
       }
+    } else {
+      // running maximum on every tile, moved only when a row's maximum
+      // exceeds it by more than kLazyLog2 (then p <= 2^kLazyLog2)
+      float mx = -__builtin_inff();
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][r]);
+      mx = wave_pair_max(mx);
+      const float m_cand = mx * c;
+      const bool grow = m_cand > m_run + kLazyLog2;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? m_cand : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+        if constexpr (ROWMFMA) {
+          const float a_rs = __int_as_float(__builtin_amdgcn_ds_bpermute(rs_src * 4, __float_as_int(alpha)));
+          lsum *= a_rs;
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      }
     }
     // From the exponentials to the last P.V MFMA this wave issues ahead of
     // the other wave on its SIMD (which is then in its K.Q^T or maximum
@@ -333,9 +362,22 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
     if constexpr (!ROWMFMA) l_run += psum;
   };
   const int steps = KSPLIT == 1 ? n_tiles : part_steps;
-  for (int t = 0; t < steps; t += 2) {
-    step(t, (SQA_LDS uint16_t*)lds_k0, (SQA_LDS uint16_t*)lds_v0, (SQA_LDS uint16_t*)lds_k1, (SQA_LDS uint16_t*)lds_v1);
-    if (t + 1 < steps) step(t + 1, (SQA_LDS uint16_t*)lds_k1, (SQA_LDS uint16_t*)lds_v1, (SQA_LDS uint16_t*)lds_k0, (SQA_LDS uint16_t*)lds_v0);
+  SQA_LDS uint16_t* const k0b = (SQA_LDS uint16_t*)lds_k0;
+  SQA_LDS uint16_t* const v0b = (SQA_LDS uint16_t*)lds_v0;
+  SQA_LDS uint16_t* const k1b = (SQA_LDS uint16_t*)lds_k1;
+  SQA_LDS uint16_t* const v1b = (SQA_LDS uint16_t*)lds_v1;
+  if constexpr (FIXED_SHIFT) {
+    // the first tile (which takes the maximum) peeled off the loop
+    if (steps > 0) step(0, k0b, v0b, k1b, v1b, true);
+    for (int t = 1; t < steps; t += 2) {
+      step(t, k1b, v1b, k0b, v0b, false);
+      if (t + 1 < steps) step(t + 1, k0b, v0b, k1b, v1b, false);
+    }
+  } else {
+    for (int t = 0; t < steps; t += 2) {
+      step(t, k0b, v0b, k1b, v1b, false);
+      if (t + 1 < steps) step(t + 1, k1b, v1b, k0b, v0b, false);
+    }
   }
 
   if constexpr (ROWMFMA) {
@@ -344,6 +386,79 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
     // each keep half of it (exact), as the v_dot2 path's partial sums
     const int src = (lane >= 16 && lane < 48) ? (lane ^ 48) : lane;
     l_run = 0.5f * __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(lsum[0])));
+  }
+
+  // Range check (fixed shift).  The first tile's maximum contributes p = 1,
+  // so the row sum is at least 1 unless that tile showed the row no key;
+  // every p is at most the row sum, so a sum of at most 2^64 and a finite O
+  // mean that no p or product overflowed.  Otherwise the wave recomputes its rows over its
+  // key range from global memory, 32 keys at a time with a running maximum
+  // (no barrier: the other waves go on).
+  if (FIXED_SHIFT && !track_max && active) {
+    const float l_pair = wave_pair_sum(l_run);
+    bool ok = l_pair >= 0.5f && l_pair <= 0x1p64f;   // false for NaN
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ok = ok && __builtin_fabsf(o[db][r]) < __builtin_inff();
+    if (__builtin_amdgcn_ballot_w64(!ok)) {
+      const int key_lo = t_first * KEYS;
+      const int key_hi = CAUSAL ? min(S, wave_last + 1) : min(S, (t_first + n_tiles) * KEYS);
+      const int last_key = min(CAUSAL ? min(my_q, S - 1) : S - 1, key_hi - 1);
+      const uint16_t* kg = p.k + (int64_t)b * S * kv_stride + g * D + half * 8;
+      const uint16_t* vg = p.v + (int64_t)b * S * kv_stride + g * D + col;
+      m_run = -__builtin_inff();
+      l_run = 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
+      for (int k0 = key_lo; k0 < key_hi; k0 += 32) {
+        // S^T block: key k0 + 8*(r/4) + 4*half + r%4 in register r
+        f32x16 sb = (f32x16){};
+        const uint16_t* kp = kg + (int64_t)min(k0 + col, S - 1) * kv_stride;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kp + ks * 16), qf[ks], sb, 0, 0, 0);
+        const int lim = last_key - k0 - 4 * half;
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (8 * (r >> 2) + (r & 3) > lim) sb[r] = -__builtin_inff();
+          mx = fmaxf(mx, sb[r]);
+        }
+        mx = wave_pair_max(mx);
+        // a lane that has seen no visible key yet keeps m = -inf and adds zeros
+        const float m_new = fmaxf(m_run, mx * c);
+        const bool seen = m_new > -__builtin_inff();
+        const float alpha = seen ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+        const float neg_m = seen ? -m_new : 0.f;
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        // P rounded to bf16, the row sum over the rounded values (as in the
+        // tile loop); O^T += V^T P^T with k-slot half*8 + e of step st at key
+        // k0 + 16*st + 4*half + e (e < 4) or k0 + 16*st + 8 + 4*half + e - 4
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          bf16x8 pb;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pb[e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sb[st * 8 + e], c, neg_m));
+            l_run += (float)pb[e];
+          }
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            bf16x8 va;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int key = min(k0 + 16 * st + (e < 4 ? 4 * half + e : 8 + 4 * half + e - 4), S - 1);
+              va[e] = __builtin_bit_cast(__bf16, vg[(int64_t)key * kv_stride + db * 32]);
+            }
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[db], 0, 0, 0);
+          }
+        }
+      }
+    }
   }
 
   if constexpr (KSPLIT > 1) {

@@ -89,6 +89,50 @@ def test_sharp_softmax(causal):
     _say(f"  {st}")
 
 
+LATE_MAX = [
+    # B, S, H_q, H_kv, d, causal: the 4-wave 64-key kernel, the 8-wave
+    # 128-key kernel (causal, ragged), the d = 64 key-split and 8-wave
+    # kernels, and d = 32 (running maximum on every tile)
+    (1, 1000, 4, 2, 128, False), (1, 1000, 4, 2, 128, True), (2, 1100, 64, 8, 128, True),
+    (1, 1000, 8, 8, 64, False), (1, 1800, 64, 64, 64, False), (1, 777, 4, 1, 32, True),
+]
+
+
+@pytest.mark.parametrize("B,S,H_q,H_kv,d,causal", LATE_MAX)
+@pytest.mark.parametrize("kval", [60.0, 100.0, 200.0])
+def test_late_maximum_far_above_the_first_tile(B, S, H_q, H_kv, d, causal, kval):
+    """One key three quarters into the sequence scores far above everything
+    before it: q[..., 0] = 4 and k[pos, :, 0] = kval add 4 * kval * scale to
+    that key's score, about 31, 51 and 102 in log2 units for kval = 60, 100
+    and 200 at d = 128.  Without the log-normaliser the d = 64 and 128
+    kernels fix the softmax shift at the first tile's maximum and see p up to
+    2^31 (kept: the row sum stays within range) or past 2^64 and the fp32
+    range (the range check sends the rows to the exact recomputation); with
+    it they keep a running maximum.  Both outputs and the log-normaliser
+    against the oracle."""
+    _say(f"late max B={B} S={S} H={H_q}/{H_kv} d={d} causal={causal} kval={kval}")
+    seed = 4700 + S + d
+    q = inputs.normal(seed, 0, (B, S, H_q, d), "bf16", 0.5)
+    k = inputs.normal(seed, 1, (B, S, H_kv, d), "bf16", 0.5)
+    v = inputs.normal(seed, 2, (B, S, H_kv, d), "bf16", 0.5)
+    pos = 3 * S // 4
+    q.reshape(-1, d)[:, 0] = np.float32(4.0).view(np.uint32) >> 16      # bf16 bits of 4.0
+    k[:, pos, :, 0] = np.float32(kval).view(np.uint32) >> 16             # 60, 100, 200: exact in bf16
+    scale = 1 / math.sqrt(d)
+    dq, dk, dv = gpu_util.to_device(q), gpu_util.to_device(k), gpu_util.to_device(v)
+    o_plain = sqa.attn_fwd(dq, dk, dv, scale=scale, causal=causal)
+    o, lse = sqa.attn_fwd(dq, dk, dv, scale=scale, causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    sc = float(np.float32(scale))
+    ref = oracle.attention(q, k, v, sc, causal=causal)
+    st = check(gpu_util.to_host_f64(o_plain), ref, "bf16", f"late max kval={kval}")
+    check(gpu_util.to_host_f64(o), ref, "bf16", f"late max kval={kval}, with lse")
+    ref_lse = oracle.lse(q, k, sc, causal=causal)
+    dl = np.abs(lse.double().cpu().numpy() - ref_lse)
+    assert dl.max() <= LSE_BOUNDS["bf16"][0], f"lse {dl.max()}"
+    _say(f"  {st} lse max {dl.max():.2e}")
+
+
 def test_tiny_f32_workload_full():
     w = WORKLOADS["tiny_f32"]
     _say("workload tiny_f32")
