@@ -33,8 +33,12 @@
 //    LDS layout XOR-swizzles 16-byte chunks by the row bits so that both the
 //    K operand reads and the transposed V reads are bank-conflict free.  LDS
 //    operand reads run several MFMAs ahead of their use.
-//  * Online softmax in the exp2 domain with a lazily moved running maximum;
-//    the row sum adds the bf16 probabilities that enter the P.V product.
+//  * Online softmax in the exp2 domain; the row sum adds the bf16
+//    probabilities that enter the P.V product.  d = 64 and 128 without the
+//    log-normaliser: the shift is the maximum of the wave's first tile and
+//    stays fixed, and a range check after the key loop sends rows whose
+//    probabilities or output left the fp32 range to an exact recomputation.
+//    Otherwise a running maximum on every tile, moved lazily.
 //  * Causal: tiles above a wave's last row are skipped, diagonal tiles are
 //    masked per element; sequence tails: key rows are clamped for the loads
 //    and masked in the scores, query rows past S are never stored.
