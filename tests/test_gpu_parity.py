@@ -133,6 +133,27 @@ def test_late_maximum_far_above_the_first_tile(B, S, H_q, H_kv, d, causal, kval)
     _say(f"  {st} lse max {dl.max():.2e}")
 
 
+@pytest.mark.parametrize("B,S,H_q,H_kv,d,causal", [
+    (1, 1000, 4, 2, 128, False), (2, 1100, 64, 8, 128, True), (1, 1000, 8, 8, 64, False),
+    (1, 1800, 64, 64, 64, False), (2, 513, 16, 4, 64, False), (1, 300, 32, 2, 64, True)])
+def test_plain_and_lse_forward_agree_bitwise(B, S, H_q, H_kv, d, causal):
+    """The plain forward fixes the softmax shift at each wave's first tile;
+    the forward that returns the log-normaliser keeps a running maximum that
+    moves only when a row's maximum grows by more than 2^8.  On N(0, 0.25)
+    inputs no later score comes near that, so the two take the same shift
+    and must give the same output bit for bit."""
+    seed = 4900 + S + d
+    q = inputs.normal(seed, 0, (B, S, H_q, d), "bf16", 0.5)
+    k = inputs.normal(seed, 1, (B, S, H_kv, d), "bf16", 0.5)
+    v = inputs.normal(seed, 2, (B, S, H_kv, d), "bf16", 0.5)
+    dq, dk, dv = gpu_util.to_device(q), gpu_util.to_device(k), gpu_util.to_device(v)
+    scale = 1 / math.sqrt(d)
+    o_plain = sqa.attn_fwd(dq, dk, dv, scale=scale, causal=causal)
+    o_lse, _ = sqa.attn_fwd(dq, dk, dv, scale=scale, causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(gpu_util.to_host_bits(o_plain), gpu_util.to_host_bits(o_lse))
+
+
 def test_tiny_f32_workload_full():
     w = WORKLOADS["tiny_f32"]
     _say("workload tiny_f32")
