@@ -338,9 +338,14 @@ def test_key_split_full_output_and_lse(B, S, H_q, H_kv, d):
     dq, dk, dv = gpu_util.to_device(q), gpu_util.to_device(k), gpu_util.to_device(v)
     for scale in (1.0 / math.sqrt(d), -0.3):
         o, lse = sqa.attn_fwd(dq, dk, dv, scale=scale, causal=False, return_lse=True)
+        # the plain forward as well: its fixed softmax shift, and key parts
+        # with no tile at the smallest sizes (they hold m = -inf, l = 0, O = 0)
+        o_plain = sqa.attn_fwd(dq, dk, dv, scale=scale, causal=False)
         torch.cuda.synchronize()
         sc = float(np.float32(scale))
-        st = check(gpu_util.to_host_f64(o), oracle.attention(q, k, v, sc), "bf16", f"key split scale={scale}")
+        ref = oracle.attention(q, k, v, sc)
+        st = check(gpu_util.to_host_f64(o), ref, "bf16", f"key split scale={scale}")
+        check(gpu_util.to_host_f64(o_plain), ref, "bf16", f"key split plain scale={scale}")
         _check_lse(lse.cpu().numpy(), oracle.lse(q, k, sc), "bf16", f"key split lse scale={scale}")
         _say(f"  scale={scale} {st}")
 
