@@ -395,9 +395,9 @@ __global__ __launch_bounds__(WAVES * 64, (fwd_min_waves_per_simd<D, WAVES, KEYS>
   // Range check (fixed shift).  The first tile's maximum contributes p = 1,
   // so the row sum is at least 1 unless that tile showed the row no key;
   // every p is at most the row sum, so a sum of at most 2^64 and a finite O
-  // mean that no p or product overflowed.  Otherwise the wave recomputes its rows over its
-  // key range from global memory, 32 keys at a time with a running maximum
-  // (no barrier: the other waves go on).
+  // mean that no p or product overflowed.  Otherwise the wave recomputes its
+  // rows over its key range from global memory, 32 keys at a time with a
+  // running maximum (no barrier: the other waves go on).
   if (FIXED_SHIFT && !track_max && active) {
     const float l_pair = wave_pair_sum(l_run);
     bool ok = l_pair >= 0.5f && l_pair <= 0x1p64f;   // false for NaN
